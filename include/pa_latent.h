@@ -1,0 +1,189 @@
+/*
+ * pa_latent.h -- C ABI of the MI355X (gfx950) paged absorbed-MLA attention library.
+ *
+ * The operation is com.microsoft::PagedAttention with kv_cache_layout = "LATENT"
+ * (absorbed multi-head latent attention, kv_num_heads = 1), as described on the
+ * docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs", module
+ * comment "LATENT semantics", and in PR #1978 ("native PagedAttention LATENT
+ * kernel for GLM-5.2 dense MLA", section "What this adds"). It has two phases,
+ * exposed as two entry points that must run in this order on one stream:
+ *
+ *   pa_latent_write      partial RoPE of each new latent key row, scattered in
+ *                        place into the paged block cache at slot_mapping[t];
+ *   pa_latent_attention  partial RoPE of each query head, then causal softmax
+ *                        attention over the block_table-addressed latent prefix,
+ *                        V = the leading v_head_size channels of the same row.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses on the current device; all tensors
+ *     are dense row-major with the shapes given below (the page's kernel refuses
+ *     strided inputs).
+ *   - 16-bit tensors (query, key, key_cache, cos_cache, sin_cache, output) share
+ *     one storage type, `dtype`. Index tensors are int32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous: they enqueue kernels and return. They never
+ *     synchronise, read device memory back, or allocate memory; launch geometry
+ *     depends only on `attrs` and `dims`, so the calls can be captured in a HIP
+ *     graph once the workspace is allocated.
+ *   - Every argument check runs before the first launch: on any error nothing
+ *     is enqueued. Errors return a pa_status and set a thread-local message read
+ *     by pa_last_error().
+ *   - The caller owns every buffer. The library allocates no device or host
+ *     memory (op-side allocation is zero, PR #1978 "Invariants held").
+ *   - Values the host cannot check without reading device memory are trusted
+ *     preconditions, as on the pages (PR #1978 review, "Non-blocking
+ *     observations"): cumulative_sequence_length[0] = 0, non-decreasing,
+ *     last entry = token_count; past_seqlens[b] + new tokens of b <=
+ *     max_blocks_per_seq * block_size; block_table entries of every block a
+ *     sequence uses lie in [0, num_blocks); slot_mapping entries are -1 or in
+ *     [0, num_blocks * block_size), distinct, and consistent with block_table;
+ *     rotary_rows > largest position. Violating them is undefined behaviour.
+ */
+#ifndef PA_LATENT_H
+#define PA_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_LATENT_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,    /* schema / geometry violation                      */
+  PA_ERR_NOT_IMPLEMENTED = 2,     /* valid request outside what this build implements */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < pa_latent_workspace_size(...)  */
+  PA_ERR_DEVICE = 4               /* a HIP runtime call failed                        */
+} pa_status;
+
+/* Storage type of the 16-bit tensors; values are the ONNX TensorProto codes. */
+typedef enum { PA_F16 = 10, PA_BF16 = 16 } pa_dtype;
+
+/*
+ * Node attributes, with the defaults the page's kernel factory applies
+ * (docs.rs page, PagedAttentionFactory::create): v_head_size 0, rotary_offset 0,
+ * do_rotary 0, rotary_interleaved 0, softcap 0, local_window_size -1, scale
+ * absent. Passed by pointer; read only during the call.
+ */
+typedef struct {
+  int32_t num_heads;          /* H >= 1 query heads (kv_num_heads is 1 by definition of LATENT) */
+  int32_t head_size;          /* hs: latent row width = key_cache.shape[3]; hs % 8 == 0         */
+  int32_t v_head_size;        /* 0 means hs; else 1 <= v_head_size <= hs                        */
+  int32_t block_size;         /* key_cache.shape[1]: a power of two >= 16                      */
+  int32_t do_rotary;          /* 0: no RoPE; nonzero: RoPE on [rotary_offset, +rotary_dim)     */
+  int32_t rotary_interleaved; /* 0: pairs (d, d + rd/2); nonzero: pairs (2i, 2i+1)             */
+  int32_t rotary_dim;         /* rd = 2 * cos_cache.shape[1]; rd % 16 == 0; ro + rd <= hs      */
+  int32_t rotary_offset;      /* ro % 8 == 0                                                   */
+  int32_t local_window_size;  /* < 0: off; W >= 0 keeps keys j with pos - j <= W               */
+  float softcap;              /* <= 0: off; else scores become softcap * tanh(s / softcap)     */
+  int32_t has_scale;          /* nonzero: use `scale`                                          */
+  float scale;                /* explicit scale; required when v_head_size != head_size,       */
+                              /* otherwise the default is 1 / sqrt(head_size)                  */
+} pa_latent_attrs;
+
+/* Host-known extents of the call's tensors. */
+typedef struct {
+  int64_t token_count;        /* T: rows of query / key / output / slot_mapping (>= 0)         */
+  int32_t batch;              /* B >= 1: sequences = past_seqlens.shape[0]                     */
+  int32_t max_blocks_per_seq; /* MB >= 1: block_table.shape[1]                                 */
+  int64_t num_blocks;         /* NB >= 1: key_cache.shape[0]                                   */
+  int64_t rotary_rows;        /* P: cos_cache.shape[0] (0 when do_rotary == 0)                 */
+} pa_latent_dims;
+
+/*
+ * Write phase (docs.rs page, "LATENT semantics", write phase; device function
+ * write_impl). For every new token t with slot = slot_mapping[t] >= 0:
+ *   key_cache row `slot` (flat [NB*bs, hs] view) = RN(RoPE(key[t], pos(t)))
+ * where b(t) is the first sequence with t < cumulative_sequence_length[b+1] and
+ * pos(t) = past_seqlens[b] + t - cumulative_sequence_length[b]. RoPE computes in
+ * float32 and only touches channels [rotary_offset, rotary_offset + rotary_dim);
+ * RN rounds to nearest even. slot = -1 leaves the cache untouched.
+ *
+ *   key                        [T, hs]            dtype
+ *   cos_cache, sin_cache       [P, rd/2]          dtype (may be NULL when do_rotary == 0)
+ *   slot_mapping               [T]                int32
+ *   cumulative_sequence_length [B + 1]            int32
+ *   past_seqlens               [B]                int32
+ *   key_cache                  [NB, bs, 1, hs]    dtype, updated in place
+ *
+ * Returns PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_NOT_IMPLEMENTED or PA_ERR_DEVICE.
+ */
+pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                          const void* key, const void* cos_cache, const void* sin_cache,
+                          const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
+                          const int32_t* past_seqlens, void* key_cache, void* stream);
+
+/*
+ * Bytes of device workspace pa_latent_attention needs for these attrs/dims on
+ * `device` (a HIP device ordinal). The workspace holds the on-device work
+ * schedule and the split-KV partial results (running max, denominator and
+ * unnormalised accumulator per row, float32). The result depends only on the
+ * arguments and the device's compute-unit count; it is written to *bytes.
+ */
+pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
+                                   pa_dtype dtype, int device, size_t* bytes);
+
+/*
+ * Read phase (docs.rs page, "LATENT semantics", read phase; device function
+ * attn_impl; two-pass softmax form per PR #1940 "PagedAttention v1 audit and
+ * MLA oracle"). For every new token t and head h:
+ *   q      = RoPE(query[t, h*hs : (h+1)*hs], pos(t))
+ *   keys   j in [0, pos(t)], and pos(t) - j <= local_window_size when that is >= 0
+ *   row_j  = key_cache row block_table[b, j / bs] * bs + j % bs
+ *   s_j    = scale * <q, row_j>;  s_j = softcap * tanh(s_j / softcap) when softcap > 0
+ *   output[t, h*vhs : (h+1)*vhs] = RN( sum_j softmax(s)_j * row_j[0 : vhs] )
+ * Must be ordered after pa_latent_write of the same step (it reads the rows
+ * that call placed).
+ *
+ *   query                      [T, H * hs]        dtype
+ *   key_cache                  [NB, bs, 1, hs]    dtype
+ *   cos_cache, sin_cache       [P, rd/2]          dtype (may be NULL when do_rotary == 0)
+ *   cumulative_sequence_length [B + 1]            int32
+ *   past_seqlens               [B]                int32
+ *   block_table                [B, MB]            int32 (entries past a sequence's last block
+ *                                                 are never read; any value, e.g. -1)
+ *   output                     [T, H * vhs]       dtype
+ *   workspace                  workspace_bytes of device memory, 256-byte aligned,
+ *                              >= pa_latent_workspace_size(...); contents on entry are
+ *                              ignored, contents on exit are unspecified.
+ *
+ * Returns PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_NOT_IMPLEMENTED,
+ * PA_ERR_WORKSPACE_TOO_SMALL or PA_ERR_DEVICE.
+ */
+pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                              const void* query, const void* key_cache, const void* cos_cache,
+                              const void* sin_cache, const int32_t* cumulative_sequence_length,
+                              const int32_t* past_seqlens, const int32_t* block_table, void* output,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_latent_attention with the split-KV partition chosen by the caller:
+ * split_kv != 0 is the automatic partition pa_latent_attention uses (work
+ * spread evenly over the device's compute units, long key ranges split and
+ * merged by a log-sum-exp combine); split_kv == 0 gives every query tile to a
+ * single workgroup (no partial results, no combine). The two agree up to
+ * float32 rounding; tests use this to check the combine.
+ */
+pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
+                                     pa_dtype dtype, const void* query, const void* key_cache,
+                                     const void* cos_cache, const void* sin_cache,
+                                     const int32_t* cumulative_sequence_length,
+                                     const int32_t* past_seqlens, const int32_t* block_table,
+                                     void* output, void* workspace, size_t workspace_bytes,
+                                     int32_t split_kv, void* stream);
+
+/* Message of the last failed call on this thread ("" after a successful call).
+ * Valid until the next call into this library on the same thread. */
+const char* pa_last_error(void);
+
+/* PA_LATENT_ABI_VERSION of the built library. */
+int32_t pa_latent_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_LATENT_H */

@@ -1,0 +1,4 @@
+// Attention instance: bf16 storage, head sizes padded to 64/32, 1 waves, 32-key tiles.
+#include "../pa_attn.cuh"
+
+PA_DEFINE_ATTN_INSTANCE(BF16, bf16, 64, 32, 1, 32)

@@ -1,0 +1,4 @@
+// Attention instance: f16 storage, head sizes padded to 192/128, 4 waves, 64-key tiles.
+#include "../pa_attn.cuh"
+
+PA_DEFINE_ATTN_INSTANCE(F16, f16, 192, 128, 4, 64)

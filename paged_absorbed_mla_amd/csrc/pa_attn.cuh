@@ -1,0 +1,548 @@
+// Read phase of paged LATENT attention on gfx950: MFMA attention over LDS-staged
+// paged latent tiles, and the split-KV combine.
+//
+// Semantics: docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs",
+// "LATENT semantics" (read phase) and device function attn_impl: per (token,
+// head), partial RoPE of the query, causal keys j <= pos with pos - j <= window
+// when a window is set, scale then softcap, online softmax with
+// corr = exp(m_old - m_new) (0 when m_old = -inf), V = leading v_head_size
+// channels of the same cached row, output acc / denom (0 when denom = 0).
+//
+// Design (not the page's: its kernel runs one 128-thread block per (token,
+// head), re-reads the whole context per head and reduces each dot product
+// with a shared-memory tree):
+//   * A workgroup owns a query tile of 32 * NW rows of one sequence (row =
+//     token_in_sequence * H + head, so consecutive rows are consecutive in
+//     `query` and `output`) and walks a contiguous range of KV tiles of KT keys.
+//   * Each KV tile (KT latent rows x HSP channels) is copied from the paged
+//     cache into LDS once, with direct global->LDS loads (no VGPR staging),
+//     double buffered, and shared by every row of the workgroup: QK^T reads all
+//     HSP channels and PV reads the first VHSP channels of the same LDS rows.
+//   * QK^T is computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: A = 32
+//     keys x 16 channels from LDS (one 16-byte read per lane), B = the wave's
+//     32 query rows, kept in registers after RoPE. The accumulator then holds
+//     one query row per lane (two lanes per row), so the softmax running max
+//     and sum live in that lane's registers and need a single cross-lane max.
+//   * PV is computed transposed too, O^T = V^T P^T: B = P^T comes straight from
+//     the S^T accumulator registers (the key order inside a 16-key step is
+//     permuted consistently on both operands), A = V^T is read from the
+//     key-major LDS tile with ds_read_b64_tr_b16 transposing loads. O^T keeps
+//     one query row per lane as well, so rescaling by the running-max
+//     correction is a per-lane multiply.
+//   * LDS rows are XOR-swizzled per 16-byte chunk (low three bits of the chunk
+//     index ^= (key & 7) ^ (key >> 3 & 1)) against bank conflicts on the
+//     column-wise reads; the global->LDS copy applies the same swizzle on the
+//     global side, so every copy instruction still writes 1 KB contiguously.
+//   * Keys outside the query tile's range are loaded from a zero page, so a
+//     masked probability (0) never meets a non-finite cache value.
+//   * Work split (flash-decoding): an on-device scheduler lays the KV tiles of
+//     all query tiles end to end and gives every workgroup an equal share.
+//     A query tile whose tiles span several workgroups gets one float32 partial
+//     (max, denominator, unnormalised accumulator) per piece, merged by the
+//     combine kernel with a log-sum-exp weighting.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// One query tile: rows [row0, row0 + nrows) of sequence b.
+struct MTile {
+  int32_t b, row0, nrows, kv_lo, kv_hi;
+  int32_t unit0;      // first global work unit (one unit = one KV tile)
+  int32_t part_base;  // first partial slot, -1 when one workgroup covers the tile
+  int32_t w_first;    // workgroup that processes the tile's first unit
+  int32_t npieces;    // workgroups that process the tile
+  int32_t pad[3];
+};
+static_assert(sizeof(MTile) == 48, "MTile layout");
+
+struct AttnParams {
+  const uint16_t* query;
+  const uint16_t* cache;
+  const uint16_t* cos_t;
+  const uint16_t* sin_t;
+  const int32_t* cumseq;
+  const int32_t* past;
+  const int32_t* bt;
+  uint16_t* out;
+  const int32_t* header;    // [0] work units U, [1] query tiles M, [2] partial slots used
+  const int32_t* wg_range;  // [grid + 1] unit range of each workgroup
+  const MTile* mt;          // [M + 1], mt[M].unit0 = U
+  const uint16_t* zero16;   // 16 zero bytes
+  float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
+  float* part_acc;          // [slots][rows][VHSP]
+  int H, hs, vhs, bs_log2, MB;
+  int ro, rd, do_rotary, interleaved, window;
+  float scale, scale_log2, softcap, softcap_inv;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Chunk swizzle of LDS row `key`: period 16 in the key, so rows 16 apart share
+// it and their addresses differ by a compile-time constant. Rows k and k + 8
+// differ in the low bit; within any aligned 8 (or 16) rows the values are
+// distinct (combined with the row parity for 16).
+__device__ __forceinline__ int lds_swizzle(int key) { return (key & 7) ^ ((key >> 3) & 1); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softcap * tanh(scale * s / softcap), returned in log2 units (times log2 e).
+// tanh(z) = 1 - 2 / (e^{2z} + 1): saturates to +-1 for large |z| (e^{2z} = inf
+// or 0) and has absolute error ~1e-7 near 0, i.e. ~softcap * 1e-7 on the score.
+__device__ __forceinline__ float softcap_log2(float s, float scale, float cap, float cap_inv) {
+  const float z = s * scale * cap_inv;
+  const float e2z = fast_exp2(z * (2.0f * kLog2e));
+  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e2z + 1.0f);
+  return cap * th * kLog2e;
+}
+
+// Scalar (s_load) read of data that no thread writes while the kernel runs:
+// block_table, sequence lengths and the schedule the previous launch wrote.
+__device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
+__device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
+  const int32_t* q = (const int32_t*)ptr;
+  MTile t;
+  t.b = ld_uniform(q + 0);
+  t.row0 = ld_uniform(q + 1);
+  t.nrows = ld_uniform(q + 2);
+  t.kv_lo = ld_uniform(q + 3);
+  t.kv_hi = ld_uniform(q + 4);
+  t.unit0 = ld_uniform(q + 5);
+  t.part_base = ld_uniform(q + 6);
+  t.w_first = ld_uniform(q + 7);
+  t.npieces = ld_uniform(q + 8);
+  t.pad[0] = t.pad[1] = t.pad[2] = 0;
+  return t;
+}
+
+// State one wavefront carries across the KV tiles of a piece: its 32 query
+// rows as MFMA B fragments, and the transposed output accumulators.
+template <typename DT, int HSP, int VHSP, int KT>
+struct WaveState {
+  static constexpr int NKK = HSP / 16;
+  static constexpr int NMT = VHSP / 32;
+  u32x4_t qf[NKK];
+  f32x16_t o[NMT];
+  float m_run, l_run;
+};
+
+// S^T = K Q^T for one LDS tile, softmax update, O^T += V^T P^T.
+template <typename DT, int HSP, int VHSP, int KT>
+__device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT>& st, const uint8_t* L, int key0,
+                                             int pos, int lo_row, bool softcap_on, const AttnParams& p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int CPR = HSP / 8;
+  constexpr int NKK = HSP / 16;
+  constexpr int NSUB = KT / 32;
+  constexpr int NMT = VHSP / 32;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // Lane reads row l32 (+32 sub), chunk 2 kk + hi. Chunks 8 apart share the
+  // swizzle, so four base addresses serve all kk with immediate offsets.
+  const int swq = lds_swizzle(l32);
+  const uint8_t* qb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) qb[r] = L + l32 * CPR * 16 + (((2 * r + hi) ^ swq) << 4);
+  f32x16_t s[NSUB];
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4_t a = *(const u32x4_t*)(qb[kk & 3] + sub * 32 * CPR * 16 + (kk >> 2) * 128);
+      acc = DT::mfma32(a, st.qf[kk], acc);
+    }
+    s[sub] = acc;
+  }
+  // Scale (and softcap) into log2 units, mask, tile max. Lane holds keys
+  // hi*4 + (e&3) + 8*(e>>2) (+32 sub) of its row l32.
+  if (softcap_on) {
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[sub][e] = softcap_log2(s[sub][e], p.scale, p.softcap, p.softcap_inv);
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) s[sub] *= p.scale_log2;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = key0 + sub * 32 + hi * 4 + (e & 3) + 8 * (e >> 2);
+      const float v = (j <= pos && j >= lo_row) ? s[sub][e] : -INFINITY;
+      s[sub][e] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // Lazy rescale: the reference max moves only when the tile max exceeds it by
+  // more than 8 (log2 units), so probabilities stay <= 2^8, and the O
+  // accumulators are rescaled only when some row of the wave moved it. The
+  // output is O / l with the same reference for both, so the result is exact.
+  const bool bump = tmax > st.m_run + 8.0f;
+  const float m_new = bump ? tmax : st.m_run;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float corr = fast_exp2(st.m_run - m_use);
+  const bool rescale = bump && (st.m_run != -INFINITY);
+  st.m_run = m_new;
+  u32x4_t pf[NSUB][2];
+  float psum = 0.0f;
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = fast_exp2(s[sub][8 * k2 + e] - m_use);
+        psum += pv[e];
+      }
+      pf[sub][k2] = pack8<DT>(pv);
+    }
+  }
+  st.l_run = st.l_run * corr + psum;
+  if (__any(rescale)) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) st.o[mt] *= corr;
+  }
+  // O^T += V^T P^T. Transposing reads: lane (g, jj, cq) supplies key row jj and
+  // channel quad cq of its 16-lane group; the group's lane i receives channel i
+  // of the 4 keys.
+  const int g = lane >> 4;
+  const int jj = (lane & 15) >> 2;
+  const int cq = lane & 3;
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  // Rows k0 = 16 step + (g >> 1) * 4 + jj and k1 = k0 + 8; the swizzle has
+  // period 16, so two rows x two chunk parities give four base addresses.
+  const int k0b = (g >> 1) * 4 + jj;
+  const int sw0 = lds_swizzle(k0b), sw1 = lds_swizzle(k0b + 8);
+  const int lcb = 2 * (g & 1) + (cq >> 1);
+  const uint8_t* vb[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    vb[0][par] = L + k0b * CPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
+    vb[1][par] = L + (k0b + 8) * CPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
+  }
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int roff = (sub * 32 + k2 * 16) * CPR * 16;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int coff = roff + (mt >> 1) * 128;
+        const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[0][mt & 1] + coff));
+        const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[1][mt & 1] + coff));
+        const u32x2_t d0 = __builtin_bit_cast(u32x2_t, r0);
+        const u32x2_t d1 = __builtin_bit_cast(u32x2_t, r1);
+        const u32x4_t a = {d0[0], d0[1], d1[0], d1[1]};
+        st.o[mt] = DT::mfma32(a, pf[sub][k2], st.o[mt]);
+      }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <typename DT, int HSP, int VHSP, int NW, int KT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void attn_kernel(AttnParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int CPR = HSP / 8;          // 16-byte chunks per LDS row
+  constexpr int TILE_CHUNKS = KT * CPR;
+  constexpr int NT = NW * 64;
+  constexpr int LOADS = TILE_CHUNKS / NT;
+  constexpr int NKK = HSP / 16;
+  constexpr int NMT = VHSP / 32;
+  constexpr int RW = NW * 32;
+  constexpr int NBLK = KT / 16;         // most blocks a tile can touch (block_size >= 16)
+  static_assert(HSP % 64 == 0 && VHSP % 32 == 0 && VHSP <= HSP, "head sizes");
+  static_assert(KT % 32 == 0 && TILE_CHUNKS % NT == 0, "tile shape");
+  constexpr int QSTRIDE = HSP + 8;      // staged query row, padded by 16 bytes against bank conflicts
+  constexpr int BUF_BYTES = TILE_CHUNKS * 16;
+  constexpr int Q_BYTES = NW * 32 * QSTRIDE * 2;
+  constexpr int LDS_BYTES = (2 * BUF_BYTES > Q_BYTES) ? 2 * BUF_BYTES : Q_BYTES;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int u = ld_uniform(p.wg_range + blockIdx.x);
+  const int u_end = ld_uniform(p.wg_range + blockIdx.x + 1);
+  if (u >= u_end) return;
+
+  // Query tile containing unit u: the last i with mt[i].unit0 <= u.
+  int i;
+  {
+    int lo = 0, hi_ = ld_uniform(p.header + 1) - 1;
+    while (lo < hi_) {
+      const int mid = (lo + hi_ + 1) >> 1;
+      if (ld_uniform(&p.mt[mid].unit0) <= u) lo = mid; else hi_ = mid - 1;
+    }
+    i = lo;
+  }
+  const bool softcap_on = p.softcap > 0.0f;
+  // Byte offset, within its cache block, of the 16-byte chunk each lane copies
+  // in copy instruction `it` (tile-independent).
+  int load_off[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) {
+    const int pidx = it * NT + (int)threadIdx.x;
+    const int k = pidx / CPR;
+    const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
+    load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.hs + lc * 8) * 2;
+  }
+
+  while (u < u_end) {
+    const MTile t = ld_uniform_tile(p.mt + i);
+    const int next0 = ld_uniform(&p.mt[i + 1].unit0);
+    const int ua = u;
+    const int ub = min(u_end, next0);
+    const int tile_a = t.kv_lo / KT + (ua - t.unit0);
+    const int tile_b = tile_a + (ub - ua);
+    const bool whole = (ua == t.unit0) && (ub == next0);
+    const int b = t.b;
+    const int cum_b = ld_uniform(p.cumseq + b);
+    const int past_b = ld_uniform(p.past + b);
+
+    const int rloc = w * 32 + l32;
+    const bool row_ok = rloc < t.nrows;
+    const int R = t.row0 + rloc;
+    const int tq = R / p.H;
+    const int h = R - tq * p.H;
+    const int pos = row_ok ? past_b + tq : -1;
+    const int lo_row = p.window >= 0 ? max(0, pos - p.window) : 0;
+    const bool wave_active = w * 32 < t.nrows;
+    const int64_t qrow = (int64_t)(cum_b + tq) * p.H + h;
+
+    WaveState<DT, HSP, VHSP, KT> st;
+    // Query rows of this wave, staged through LDS (free between pieces),
+    // RoPE'd there with one thread per rotary pair, read back as fragments
+    // (row l32, channels 16 kk + 8 hi .. + 8).
+    {
+      uint16_t* qs = (uint16_t*)lds_raw + w * 32 * QSTRIDE;
+      constexpr int QCH = HSP / 8;
+      for (int idx = lane; idx < 32 * QCH; idx += 64) {
+        const int r = idx / QCH;
+        const int c0 = (idx - r * QCH) * 8;
+        const int rl = w * 32 + r;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (rl < t.nrows && c0 < p.hs) {
+          const int Rr = t.row0 + rl;
+          const int tr = Rr / p.H;
+          const int64_t gq = (int64_t)(cum_b + tr) * p.H + (Rr - tr * p.H);
+          v = *(const u32x4_t*)(p.query + gq * p.hs + c0);
+        }
+        *(u32x4_t*)(qs + r * QSTRIDE + c0) = v;
+      }
+      __syncthreads();
+      if (p.do_rotary) {
+        const int half = p.rd >> 1;
+        for (int idx = lane; idx < 32 * half; idx += 64) {
+          const int r = idx / half;
+          const int k = idx - r * half;
+          const int rl = w * 32 + r;
+          if (rl >= t.nrows) continue;
+          const int posr = past_b + (t.row0 + rl) / p.H;
+          const int d1 = p.interleaved ? p.ro + 2 * k : p.ro + k;
+          const int d2 = p.interleaved ? d1 + 1 : d1 + half;
+          const float c = DT::to_f32(p.cos_t[(int64_t)posr * half + k]);
+          const float sn = DT::to_f32(p.sin_t[(int64_t)posr * half + k]);
+          const float x1 = DT::to_f32(qs[r * QSTRIDE + d1]);
+          const float x2 = DT::to_f32(qs[r * QSTRIDE + d2]);
+          qs[r * QSTRIDE + d1] = (uint16_t)DT::from_f32(x1 * c - x2 * sn);
+          qs[r * QSTRIDE + d2] = (uint16_t)DT::from_f32(x2 * c + x1 * sn);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        st.qf[kk] = *(const u32x4_t*)(qs + l32 * QSTRIDE + 16 * kk + 8 * hi);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) st.o[mt] = f32x16_t{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.0f;
+
+    // Copy KV tile `tile` into LDS buffer `bufi`: 16 bytes per lane, global ->
+    // LDS directly. Copy instruction (it, wave) fills 64 consecutive 16-byte
+    // LDS slots, which always belong to rows of one cache block (block_size *
+    // CPR is a multiple of 64), so its source is a scalar block base plus the
+    // lane's precomputed offset. Slots of keys outside [kv_lo, kv_hi) or
+    // channels >= hs are zero-filled instead (boundary tiles only).
+    auto issue = [&](int tile, int bufi) {
+      const int key0 = tile * KT;
+      const int blk0 = key0 >> p.bs_log2;
+      const int in_blk = key0 & ((1 << p.bs_log2) - 1);      // nonzero only when block_size > KT
+      int blks[NBLK];
+#pragma unroll
+      for (int e = 0; e < NBLK; ++e) blks[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
+      const bool interior = key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP;
+      uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
+#pragma unroll
+      for (int it = 0; it < LOADS; ++it) {
+        const int kfirst = ((it * NW + w) * 64) / CPR;        // wave-uniform first key of the slots
+        const int e = kfirst >> p.bs_log2;
+        int blk = blks[0];
+#pragma unroll
+        for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
+        const uint16_t* base = p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.hs;
+        uint8_t* dst = dst0 + it * NT * 16;
+        if (interior) {
+          __builtin_amdgcn_global_load_lds((const uint8_t*)base + load_off[it], dst, 16, 0, 0);
+        } else {
+          const int pidx = it * NT + (int)threadIdx.x;
+          const int k = pidx / CPR;
+          const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
+          const int j = key0 + k;
+          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs)
+            __builtin_amdgcn_global_load_lds((const uint8_t*)base + load_off[it], dst, 16, 0, 0);
+          else
+            *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+
+    issue(tile_a, 0);
+    if (wave_active) {
+      for (int tt = tile_a; tt < tile_b; ++tt) {
+        const int bufi = (tt - tile_a) & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
+        tile_compute<DT, HSP, VHSP, KT>(st, lds_raw + bufi * BUF_BYTES, tt * KT, pos, lo_row, softcap_on, p);
+      }
+    } else {
+      for (int tt = tile_a; tt < tile_b; ++tt) {
+        const int bufi = (tt - tile_a) & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
+      }
+    }
+    __syncthreads();
+
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    if (whole) {
+      if (row_ok) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t* orow = p.out + qrow * p.vhs;
+        const bool vec_ok = (p.vhs & 3) == 0;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int c0 = mt * 32 + hi * 4 + 8 * grp;
+            const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
+            const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
+            const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
+            const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
+            if (vec_ok) {
+              if (c0 < p.vhs) *(u32x2_t*)(orow + c0) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+            } else {
+              if (c0 + 0 < p.vhs) orow[c0 + 0] = (uint16_t)e0;
+              if (c0 + 1 < p.vhs) orow[c0 + 1] = (uint16_t)e1;
+              if (c0 + 2 < p.vhs) orow[c0 + 2] = (uint16_t)e2;
+              if (c0 + 3 < p.vhs) orow[c0 + 3] = (uint16_t)e3;
+            }
+          }
+        }
+      }
+    } else {
+      const int64_t slot = (int64_t)t.part_base + ((int)blockIdx.x - t.w_first);
+      if (hi == 0) {
+        float* ml = p.part_ml + (slot * RW + rloc) * 2;
+        ml[0] = st.m_run;
+        ml[1] = l_tot;
+      }
+      float* acc = p.part_acc + (slot * RW + rloc) * VHSP;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int c0 = mt * 32 + hi * 4 + 8 * grp;
+          *(f32x4_t*)(acc + c0) =
+              f32x4_t{st.o[mt][4 * grp], st.o[mt][4 * grp + 1], st.o[mt][4 * grp + 2], st.o[mt][4 * grp + 3]};
+        }
+      }
+    }
+    u = ub;
+    ++i;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Merge the partials of every query tile that several workgroups processed:
+// with M = max_i m_i (log2 domain) and w_i = 2^(m_i - M),
+// out = sum_i w_i acc_i / sum_i w_i l_i, rounded to nearest even.
+template <typename DT, int VHSP, int RW>
+__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
+  const int i = blockIdx.x;
+  if (i >= p.header[1]) return;
+  const MTile t = p.mt[i];
+  if (t.npieces <= 1) return;
+  constexpr int C4 = VHSP / 4;
+  const int cum_b = p.cumseq[t.b];
+  for (int idx = threadIdx.x; idx < t.nrows * C4; idx += 256) {
+    const int r = idx / C4;
+    const int c0 = (idx - r * C4) * 4;
+    if (c0 >= p.vhs) continue;
+    float mx = -INFINITY;
+    for (int q = 0; q < t.npieces; ++q)
+      mx = fmaxf(mx, p.part_ml[((int64_t)(t.part_base + q) * RW + r) * 2]);
+    float den = 0.0f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < t.npieces; ++q) {
+      const int64_t sr = (int64_t)(t.part_base + q) * RW + r;
+      const float m = p.part_ml[sr * 2];
+      const float wq = (m == -INFINITY) ? 0.0f : fast_exp2(m - mx);
+      den += wq * p.part_ml[sr * 2 + 1];
+      const f32x4_t a = *(const f32x4_t*)(p.part_acc + sr * VHSP + c0);
+      acc += wq * a;
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    const int R = t.row0 + r;
+    const int tq = R / p.H;
+    const int h = R - tq * p.H;
+    uint16_t* orow = p.out + ((int64_t)(cum_b + tq) * p.H + h) * p.vhs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (c0 + k < p.vhs) orow[c0 + k] = (uint16_t)DT::from_f32(acc[k] * inv);
+  }
+}
+
+typedef hipError_t (*AttnLaunchFn)(const AttnParams&, int, bool, int, hipStream_t);
+typedef hipError_t (*AttnOccFn)(int*);
+
+}  // namespace pa
+
+#define PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, SUF) attn_##DTN##_##HSP##_##VHSP##_##NW##_##KT##_##SUF
+#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT)                                                 \
+  namespace pa {                                                                                            \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                              \
+    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT>;                                            \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0);  \
+  }                                                                                                         \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,         \
+                                                        int cgrid, hipStream_t s) {                           \
+    attn_kernel<DT, HSP, VHSP, NW, KT><<<grid, NW * 64, 0, s>>>(p);                                         \
+    hipError_t e = hipGetLastError();                                                                       \
+    if (e != hipSuccess || !combine) return e;                                                              \
+    combine_kernel<DT, VHSP, NW * 32><<<cgrid, 256, 0, s>>>(p);                                              \
+    return hipGetLastError();                                                                               \
+  }                                                                                                         \
+  }
+#define PA_DECLARE_ATTN_INSTANCE(DTN, HSP, VHSP, NW, KT)                                                    \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams&, int, bool, int, hipStream_t);    \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int*);

@@ -1,0 +1,323 @@
+// On-device work scheduler for the read phase, instance table, workspace plan
+// and launch sequence (scheduler -> attention -> combine) on the caller's stream.
+//
+// The launch geometry depends only on host-known shapes (token count, batch,
+// compute units); everything that depends on sequence lengths is derived on
+// the device from cumulative_sequence_length / past_seqlens, with no readback
+// (docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs", module
+// comment "Capture safety": geometry fixed by tensor shapes, positions and
+// blocks resolved on device).
+#include "pa_attn.cuh"
+
+#include <algorithm>
+#include <mutex>
+#include <map>
+#include <tuple>
+
+namespace pa {
+
+struct SchedParams {
+  const int32_t* cumseq;
+  const int32_t* past;
+  int B, H, RW, KT, window, grid, split_kv;
+  int64_t max_mtiles, part_cap;
+  int32_t* header;
+  int32_t* wg_range;
+  int32_t* seq_base;
+  MTile* mt;
+  uint32_t* zero16;
+};
+
+constexpr int kSchedThreads = 1024;
+
+// Exclusive prefix sum over n values get(i), written with put(i, prefix);
+// returns the total. Every thread of the block must call it.
+template <typename Get, typename Put>
+__device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
+  __shared__ int64_t wave_sums[kSchedThreads / 64];
+  __shared__ int64_t chunk_total;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < n; base += kSchedThreads) {
+    const int64_t idx = base + threadIdx.x;
+    const int64_t v = idx < n ? get(idx) : 0;
+    int64_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_sums[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t run = 0;
+      for (int k = 0; k < kSchedThreads / 64; ++k) {
+        const int64_t s = wave_sums[k];
+        wave_sums[k] = run;
+        run += s;
+      }
+      chunk_total = run;
+    }
+    __syncthreads();
+    if (idx < n) put(idx, carry + wave_sums[wave] + x - v);
+    carry += chunk_total;
+    __syncthreads();
+  }
+  return carry;
+}
+
+// Workgroup w covers units [wg_range[w], wg_range[w+1]); the one that holds
+// unit u is the last w with wg_range[w] <= u.
+__device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int u) {
+  int lo = 0, hi = grid - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wg_range[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
+  if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
+  // A. query tiles per sequence, prefix-summed into seq_base.
+  const int64_t M_all = block_exclusive_scan(
+      p.B,
+      [&](int64_t b) -> int64_t {
+        const int64_t rows = (int64_t)(p.cumseq[b + 1] - p.cumseq[b]) * p.H;
+        return (rows + p.RW - 1) / p.RW;
+      },
+      [&](int64_t b, int64_t v) { p.seq_base[b] = (int32_t)v; });
+  // M cannot exceed max_mtiles when cumseq[B] = T (a precondition); clamp so a
+  // violated precondition cannot write past the tile table.
+  const int64_t M = min(M_all, p.max_mtiles);
+  if (threadIdx.x == 0) p.seq_base[p.B] = (int32_t)M_all;
+  __syncthreads();
+  // B. describe every query tile; its KV tile count goes to unit0 for now.
+  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
+    int lo = 0, hi = p.B - 1;  // last b with seq_base[b] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq_base[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int rows = (p.cumseq[b + 1] - p.cumseq[b]) * p.H;
+    const int row0 = (int)(i - p.seq_base[b]) * p.RW;
+    const int nrows = min(p.RW, rows - row0);
+    const int pos0 = p.past[b] + row0 / p.H;
+    const int pos1 = p.past[b] + (row0 + nrows - 1) / p.H;
+    const int kv_hi = pos1 + 1;
+    const int kv_lo = p.window >= 0 ? max(0, pos0 - p.window) : 0;
+    MTile t;
+    t.b = b;
+    t.row0 = row0;
+    t.nrows = nrows;
+    t.kv_lo = kv_lo;
+    t.kv_hi = kv_hi;
+    t.unit0 = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
+    t.part_base = -1;
+    t.w_first = 0;
+    t.npieces = 1;
+    t.pad[0] = t.pad[1] = t.pad[2] = 0;
+    p.mt[i] = t;
+  }
+  __syncthreads();
+  // C. units: prefix sum of KV tiles.
+  const int64_t U = block_exclusive_scan(
+      M, [&](int64_t i) -> int64_t { return p.mt[i].unit0; },
+      [&](int64_t i, int64_t v) { p.mt[i].unit0 = (int32_t)v; });
+  if (threadIdx.x == 0) {
+    MTile s = {};
+    s.unit0 = (int32_t)U;
+    p.mt[M] = s;
+  }
+  __syncthreads();
+  // D. unit range of every workgroup.
+  // Empty ranges only ever sit at the end, so the workgroups that share a query
+  // tile are consecutive and each of them writes its partial slot.
+  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
+    int32_t v;
+    if (!p.split_kv) v = p.mt[min((int64_t)w, M)].unit0;
+    else if (U >= p.grid) v = (int32_t)(((int64_t)w * U) / p.grid);
+    else v = (int32_t)min((int64_t)w, U);
+    p.wg_range[w] = v;
+  }
+  __syncthreads();
+  // E. pieces per query tile.
+  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
+    const int w0 = wg_of_unit(p.wg_range, p.grid, p.mt[i].unit0);
+    const int w1 = wg_of_unit(p.wg_range, p.grid, p.mt[i + 1].unit0 - 1);
+    p.mt[i].w_first = w0;
+    p.mt[i].npieces = w1 - w0 + 1;
+  }
+  __syncthreads();
+  // F. partial slots for the tiles that several workgroups share.
+  const int64_t slots = block_exclusive_scan(
+      M, [&](int64_t i) -> int64_t { const int n = p.mt[i].npieces; return n > 1 ? n : 0; },
+      [&](int64_t i, int64_t v) { p.mt[i].part_base = p.mt[i].npieces > 1 ? (int32_t)v : -1; });
+  if (threadIdx.x == 0) {
+    p.header[0] = (int32_t)U;
+    p.header[1] = (int32_t)M;
+    p.header[2] = (int32_t)slots;
+    p.header[3] = (slots > p.part_cap || M > p.max_mtiles) ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Instance table
+// ---------------------------------------------------------------------------
+
+PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 64, 32, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(f16, 64, 32, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(bf16, 64, 32, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 64, 32, 4, 64)
+
+struct InstanceEntry {
+  int dtype, hsp, vhsp, nw, kt;
+  AttnLaunchFn launch;
+  AttnOccFn occ;
+};
+
+#define PA_ENTRY(DTC, DTN, HSP, VHSP, NW, KT)                                               \
+  {DTC, HSP, VHSP, NW, KT, &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch),                     \
+   &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)}
+
+static const InstanceEntry kInstances[] = {
+    PA_ENTRY(16, bf16, 576, 512, 4, 64), PA_ENTRY(10, f16, 576, 512, 4, 64),
+    PA_ENTRY(16, bf16, 576, 512, 1, 64), PA_ENTRY(10, f16, 576, 512, 1, 64),
+    PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
+    PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
+    PA_ENTRY(16, bf16, 64, 32, 1, 32),   PA_ENTRY(10, f16, 64, 32, 1, 32),
+    PA_ENTRY(16, bf16, 64, 32, 4, 64),   PA_ENTRY(10, f16, 64, 32, 4, 64),
+};
+
+static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
+  for (const auto& e : kInstances)
+    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.nw && e.kt == c.kt) return &e;
+  return nullptr;
+}
+
+bool choose_config(const CallGeom& g, AttnConfig* cfg) {
+  // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
+  if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
+  else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 64; }
+  else return false;
+  // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
+  const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
+  cfg->nw = rows_per_seq >= 96 ? 4 : 1;
+  if (cfg->hsp == 64 && cfg->nw == 4) cfg->kt = 64;   // staged query rows need 2 tiles >= 32 * nw rows
+  return find_instance(g.dtype, *cfg) != nullptr;
+}
+
+hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, int* blocks_per_cu) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int, int>, int> cache;
+  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.nw, cfg.kt);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) { *blocks_per_cu = it->second; return hipSuccess; }
+  }
+  const InstanceEntry* e = find_instance(g.dtype, cfg);
+  if (!e) return hipErrorInvalidValue;
+  int n = 0;
+  hipError_t err = e->occ(&n);
+  if (err != hipSuccess) return err;
+  n = std::max(n, 1);
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = n;
+  *blocks_per_cu = n;
+  return hipSuccess;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv) {
+  WsLayout L{};
+  const int RW = cfg.rows();
+  L.max_mtiles = (g.T * g.H + RW - 1) / RW + std::min<int64_t>(g.B, g.T);
+  const int64_t g_split = (int64_t)num_cus * blocks_per_cu;
+  L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
+  L.part_cap = split_kv ? L.max_mtiles + L.grid : 0;
+  size_t off = 0;
+  L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
+  L.off_zero = off; off = align256(off + 16);
+  L.off_wg_range = off; off = align256(off + (size_t)(L.grid + 1) * sizeof(int32_t));
+  L.off_seq_base = off; off = align256(off + (size_t)(g.B + 1) * sizeof(int32_t));
+  L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
+  L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
+  L.off_part_acc = off; off = align256(off + (size_t)L.part_cap * RW * cfg.vhsp * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
+                            const void* query, const void* cache, const void* cos_t, const void* sin_t,
+                            const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* out,
+                            void* workspace, hipStream_t stream) {
+  if (g.T == 0) return hipSuccess;
+  const InstanceEntry* e = find_instance(g.dtype, cfg);
+  if (!e) return hipErrorInvalidValue;
+  uint8_t* wsb = (uint8_t*)workspace;
+  SchedParams sp;
+  sp.cumseq = cumseq;
+  sp.past = past;
+  sp.B = g.B;
+  sp.H = g.H;
+  sp.RW = cfg.rows();
+  sp.KT = cfg.kt;
+  sp.window = g.window;
+  sp.grid = ws.grid;
+  sp.split_kv = split_kv ? 1 : 0;
+  sp.max_mtiles = ws.max_mtiles;
+  sp.part_cap = ws.part_cap;
+  sp.header = (int32_t*)(wsb + ws.off_header);
+  sp.wg_range = (int32_t*)(wsb + ws.off_wg_range);
+  sp.seq_base = (int32_t*)(wsb + ws.off_seq_base);
+  sp.mt = (MTile*)(wsb + ws.off_mtiles);
+  sp.zero16 = (uint32_t*)(wsb + ws.off_zero);
+  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(sp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  AttnParams ap;
+  ap.query = (const uint16_t*)query;
+  ap.cache = (const uint16_t*)cache;
+  ap.cos_t = (const uint16_t*)cos_t;
+  ap.sin_t = (const uint16_t*)sin_t;
+  ap.cumseq = cumseq;
+  ap.past = past;
+  ap.bt = block_table;
+  ap.out = (uint16_t*)out;
+  ap.header = sp.header;
+  ap.wg_range = sp.wg_range;
+  ap.mt = sp.mt;
+  ap.zero16 = (const uint16_t*)sp.zero16;
+  ap.part_ml = (float*)(wsb + ws.off_part_ml);
+  ap.part_acc = (float*)(wsb + ws.off_part_acc);
+  ap.H = g.H;
+  ap.hs = g.hs;
+  ap.vhs = g.vhs;
+  ap.bs_log2 = g.bs_log2;
+  ap.MB = g.MB;
+  ap.ro = g.ro;
+  ap.rd = g.rd;
+  ap.do_rotary = g.do_rotary;
+  ap.interleaved = g.interleaved;
+  ap.window = g.window;
+  ap.scale = g.scale;
+  ap.scale_log2 = g.scale * kLog2e;
+  ap.softcap = g.softcap > 0.0f ? g.softcap : 0.0f;
+  ap.softcap_inv = g.softcap > 0.0f ? 1.0f / g.softcap : 0.0f;
+  return e->launch(ap, ws.grid, split_kv, (int)ws.max_mtiles, stream);
+}
+
+}  // namespace pa

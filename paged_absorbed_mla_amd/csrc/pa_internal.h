@@ -1,0 +1,59 @@
+// Host-side interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Resolved, validated parameters of one call (host copy).
+struct CallGeom {
+  int dtype;            // 10 = f16, 16 = bf16
+  int H, hs, vhs, bs, bs_log2;
+  int do_rotary, interleaved, rd, ro;
+  int window;           // < 0 = off
+  float softcap;        // <= 0 = off
+  float scale;
+  int64_t T;
+  int B, MB;
+  int64_t NB, P;
+};
+
+// Write phase: one launch.
+hipError_t launch_write(const CallGeom& g, const void* key, const void* cos_t, const void* sin_t,
+                        const int32_t* slot, const int32_t* cumseq, const int32_t* past, void* cache,
+                        hipStream_t stream);
+
+// Attention kernel configuration chosen for a call.
+struct AttnConfig {
+  int hsp, vhsp;   // padded head sizes of the compiled instance
+  int nw;          // waves per workgroup; rows per workgroup = 32 * nw
+  int kt;          // keys per LDS tile
+  int rows() const { return 32 * nw; }
+};
+
+// Chooses the instance for a geometry; returns false when no compiled instance fits.
+bool choose_config(const CallGeom& g, AttnConfig* cfg);
+
+// Workspace layout derived from the geometry, the config and the grid size.
+struct WsLayout {
+  int64_t max_mtiles;   // upper bound on query tiles
+  int grid;             // workgroups of the attention launch
+  int64_t part_cap;     // partial-result slots
+  size_t off_header, off_wg_range, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  size_t total;
+};
+
+// Workgroups the attention kernel can keep resident per CU (cached per device).
+hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, int* blocks_per_cu);
+
+WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv);
+
+// Attention phase: schedule, attention, combine (three launches).
+hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
+                            const void* query, const void* cache, const void* cos_t, const void* sin_t,
+                            const int32_t* cumseq, const int32_t* past, const int32_t* block_table,
+                            void* out, void* workspace, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,63 @@
+// Write phase: partial RoPE of each new latent key row, scattered in place into
+// the paged block cache at slot_mapping[t] (-1 skips).
+//
+// Semantics: docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs",
+// "LATENT semantics" (write phase) and device function write_impl. The page's
+// kernel runs one thread per element with a linear sequence scan per element;
+// here one wavefront owns one token row: the (batch, position) lookup and the
+// slot read happen once per row, and the row moves as coalesced 16-byte
+// chunks (8 channels per lane).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kWriteWaves = 4;
+
+template <typename DT>
+__global__ __launch_bounds__(kWriteWaves * 64) void write_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ cos_t, const uint16_t* __restrict__ sin_t,
+    const int32_t* __restrict__ slot_mapping, const int32_t* __restrict__ cumseq,
+    const int32_t* __restrict__ past, uint16_t* __restrict__ cache, int64_t T, int hs, int ro, int rd,
+    int do_rotary, int interleaved, int B) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kWriteWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int slot = slot_mapping[t];
+  if (slot < 0) return;
+  const int b = find_seq(cumseq, B, t);
+  const int64_t pos = (int64_t)past[b] + (t - (int64_t)cumseq[b]);
+  const uint16_t* row = key + t * hs;
+  uint16_t* dst = cache + (int64_t)slot * hs;
+  const int nchunks = hs >> 3;
+  for (int c = lane; c < nchunks; c += 64) {
+    const int c0 = c << 3;
+    u32x4_t v = *(const u32x4_t*)(row + c0);
+    if (do_rotary && c0 >= ro && c0 < ro + rd) {
+      float x[8];
+      unpack8<DT>(v, x);
+      rope_chunk<DT>(x, row, c0, ro, rd, interleaved, pos, cos_t, sin_t);
+      v = pack8<DT>(x);
+    }
+    *(u32x4_t*)(dst + c0) = v;
+  }
+}
+
+hipError_t launch_write(const CallGeom& g, const void* key, const void* cos_t, const void* sin_t,
+                        const int32_t* slot, const int32_t* cumseq, const int32_t* past, void* cache,
+                        hipStream_t stream) {
+  if (g.T == 0) return hipSuccess;
+  const int64_t blocks = (g.T + kWriteWaves - 1) / kWriteWaves;
+  dim3 grid((unsigned)blocks), block(kWriteWaves * 64);
+  if (g.dtype == 16)
+    write_kernel<BF16><<<grid, block, 0, stream>>>((const uint16_t*)key, (const uint16_t*)cos_t,
+                                                   (const uint16_t*)sin_t, slot, cumseq, past, (uint16_t*)cache,
+                                                   g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B);
+  else
+    write_kernel<F16><<<grid, block, 0, stream>>>((const uint16_t*)key, (const uint16_t*)cos_t,
+                                                  (const uint16_t*)sin_t, slot, cumseq, past, (uint16_t*)cache,
+                                                  g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B);
+  return hipGetLastError();
+}
+
+}  // namespace pa

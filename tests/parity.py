@@ -1,0 +1,82 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the CPU oracle).
+
+Tolerances: outputs within max-abs 2e-3 (float16) / 1.6e-2 (bfloat16) of the
+oracle, and, because max-abs alone is weak where outputs are small, relative
+Frobenius error <= 2e-3 (float16) / 1e-2 (bfloat16). Written cache rows: bit
+exact outside the rotary channels, within 1 ulp of the storage type inside
+them (the kernel rotates in float32, the oracle in float64; both round to
+nearest even). Untouched cache rows: bit exact.
+"""
+import numpy as np
+
+from oracle import paged_latent as orc
+
+MAX_ABS = {"f16": 2e-3, "bf16": 1.6e-2}
+REL_FRO = {"f16": 2e-3, "bf16": 1e-2}
+
+
+def ordered(bits: np.ndarray) -> np.ndarray:
+    """Map 16-bit float patterns to integers whose order and spacing follow the
+    floats' (sign-magnitude to two's complement); +0 and -0 both map to 0."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp_distance(a_bits, b_bits) -> np.ndarray:
+    return np.abs(ordered(np.asarray(a_bits)) - ordered(np.asarray(b_bits)))
+
+
+def check_write(w: dict, gpu_cache: np.ndarray, ref_cache: np.ndarray, before: np.ndarray):
+    hs = w["attrs"]["head_size"]
+    g = gpu_cache.reshape(-1, hs)
+    r = ref_cache.reshape(-1, hs)
+    b0 = before.reshape(-1, hs)
+    slots = w["slot_mapping"]
+    written = np.unique(slots[slots >= 0])
+    untouched = np.setdiff1d(np.arange(g.shape[0]), written)
+    assert np.array_equal(g[untouched], b0[untouched]), "rows without a slot changed"
+    a = w["attrs"]
+    rot = np.zeros(hs, dtype=bool)
+    if a["do_rotary"]:
+        rot[a["rotary_offset"]:a["rotary_offset"] + a["rotary_dim"]] = True
+    gw, rw = g[written], r[written]
+    assert np.array_equal(gw[:, ~rot], rw[:, ~rot]), "non-rotary channels of written rows differ"
+    if rot.any():
+        d = ulp_distance(gw[:, rot], rw[:, rot])
+        assert d.max() <= 1, f"rotary channels differ by {d.max()} ulp"
+
+
+def check_output(dtype: str, got: np.ndarray, ref: np.ndarray, rows=None, what=""):
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref)) / den if den > 0 else float(np.linalg.norm(got))
+    assert max_abs <= MAX_ABS[dtype], f"{what}: max-abs {max_abs:.3e} > {MAX_ABS[dtype]}"
+    assert rel <= REL_FRO[dtype], f"{what}: relative Frobenius {rel:.3e} > {REL_FRO[dtype]}"
+    # negative control: the same check must reject an all-zero output
+    zero_rel = 1.0 if den > 0 else 0.0
+    assert den == 0 or zero_rel > REL_FRO[dtype]
+    return max_abs, rel
+
+
+def sample_tokens(w: dict, n: int, seed: int = 0) -> np.ndarray:
+    """Sampled tokens: first and last token of the batch, last token of each of a few
+    sequences, plus random ones."""
+    T = w["dims"]["token_count"]
+    rng = np.random.default_rng(seed)
+    cum = w["cumulative_sequence_length"]
+    picks = {0, T - 1}
+    for b in rng.choice(len(cum) - 1, size=min(n, len(cum) - 1), replace=False):
+        if cum[b + 1] > cum[b]:
+            picks.add(int(cum[b + 1] - 1))
+    picks.update(int(x) for x in rng.choice(T, size=min(n, T), replace=False))
+    return np.array(sorted(picks))
+
+
+def oracle(w: dict, tokens=None):
+    cache = orc.write_phase(w)
+    return cache, orc.attention(w, cache, tokens=tokens)

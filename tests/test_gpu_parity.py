@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Each case prints its name and shape before touching the GPU. Element-wise
+parity runs at sizes the oracle finishes in seconds (several tiles, ragged
+tails); the five full-size workloads run in the launch configuration the
+benchmark times and are compared on sampled tokens.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import paged_latent as orc
+from paged_absorbed_mla_amd import workloads as wl
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _dev(w, **kw):
+    from paged_absorbed_mla_amd.device import DeviceWorkload
+    print(f"\n[case] {w.get('name')} dtype={w['dtype']} dims={w['dims']}", flush=True)
+    return DeviceWorkload(w, **kw)
+
+
+def _run(w, split_kv=None):
+    torch = _torch()
+    d = _dev(w)
+    before = w["key_cache"].copy()
+    d.write()
+    d.attention(split_kv=split_kv)
+    torch.cuda.synchronize()
+    return d, before
+
+
+# ---------------------------------------------------------------------------
+# The five workloads, scaled so the oracle checks every element
+# ---------------------------------------------------------------------------
+
+SMALL = [("c1", 1), ("c2", 4), ("c3", 8), ("c4", 8), ("c5", 4)]
+
+
+@pytest.mark.parametrize("cfg,sd", SMALL, ids=[f"{c}/{s}" for c, s in SMALL])
+def test_parity_elementwise(cfg, sd):
+    w = wl.make(cfg, scale_down=sd)
+    d, before = _run(w)
+    ref_cache, ref_out = parity.oracle(w)
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    mx, rel = parity.check_output(w["dtype"], d.output_f64(), ref_out, what=cfg)
+    print(f"[result] {cfg}/{sd}: max-abs {mx:.3e} rel {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
+def test_parity_full_size_sampled(cfg):
+    w = wl.make(cfg)
+    d, before = _run(w)
+    toks = parity.sample_tokens(w, 6, seed=1)
+    ref_cache, ref_out = parity.oracle(w, tokens=toks)
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    mx, rel = parity.check_output(w["dtype"], d.output_f64(), ref_out, rows=toks, what=cfg)
+    print(f"[result] {cfg} full, {len(toks)} tokens: max-abs {mx:.3e} rel {rel:.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,sd", [("c4", 8), ("c5", 4), ("c3", 8)])
+def test_split_partition_invariance(cfg, sd):
+    """Automatic split-KV vs one workgroup per query tile: equal up to float32
+    rounding (at most 1 ulp of the storage type per element, rarely)."""
+    torch = _torch()
+    w = wl.make(cfg, scale_down=sd)
+    d = _dev(w)
+    d.write()
+    d.attention(split_kv=True)
+    torch.cuda.synchronize()
+    a = d.output.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    d.attention(split_kv=False)
+    torch.cuda.synchronize()
+    b = d.output.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    dist = parity.ulp_distance(a, b)
+    assert dist.max() <= 2 and (dist > 0).mean() < 0.01, (dist.max(), (dist > 0).mean())
+
+
+def _permute(w, seed):
+    rng = np.random.default_rng(seed)
+    NB, bs = w["key_cache"].shape[0], w["key_cache"].shape[1]
+    perm = rng.permutation(NB)
+    w2 = dict(w)
+    c = np.empty_like(w["key_cache"])
+    c[perm] = w["key_cache"]
+    w2["key_cache"] = c
+    bt = w["block_table"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    w2["block_table"] = bt
+    s = w["slot_mapping"].copy()
+    ok = s >= 0
+    s[ok] = perm[s[ok] // bs] * bs + s[ok] % bs
+    w2["slot_mapping"] = s
+    return w2
+
+
+@pytest.mark.parametrize("cfg,sd", [("c1", 1), ("c5", 4), ("c4", 8)])
+def test_block_permutation_bit_identical(cfg, sd):
+    w = wl.make(cfg, scale_down=sd)
+    torch = _torch()
+    d1, _ = _run(w)
+    d2, _ = _run(_permute(w, 7))
+    o1 = d1.output.view(torch.int16).cpu().numpy()
+    o2 = d2.output.view(torch.int16).cpu().numpy()
+    assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("cfg,sd", [("c1", 1), ("c5", 4), ("c2", 4)])
+def test_poisoned_unreachable_rows_do_not_leak(cfg, sd):
+    """Rows no visible key can reach hold NaN; outputs must be unchanged and finite."""
+    w = wl.make(cfg, scale_down=sd)
+    wp = wl.make(cfg, scale_down=sd, poison=True)
+    d1, _ = _run(w)
+    d2, _ = _run(wp)
+    o2 = d2.output_f64()
+    assert np.all(np.isfinite(o2))
+    assert np.array_equal(d1.output_f64(), o2)
+
+
+def test_repeat_is_deterministic():
+    torch = _torch()
+    w = wl.make("c5", scale_down=4)
+    d = _dev(w)
+    d.write()
+    d.attention()
+    torch.cuda.synchronize()
+    a = d.output_f64()
+    for _ in range(3):
+        d.write()          # idempotent: rewrites the same rows
+        d.attention()
+    torch.cuda.synchronize()
+    assert np.array_equal(a, d.output_f64())
+
+
+# ---------------------------------------------------------------------------
+# Edge cases of the method
+# ---------------------------------------------------------------------------
+
+def _spec(**kw):
+    base = dict(name="edge", dtype="bf16", past=[0, 37, 5], new=[1, 3, 70], num_heads=4, head_size=64,
+                v_head_size=32, rotary_dim=16, rotary_offset=48, block_size=16, scale=0.125, seed=11)
+    base.update(kw)
+    return wl.Spec(**base)
+
+
+def _edge(spec, split_kv=None):
+    w = wl.build(spec)
+    d, before = _run(w, split_kv=split_kv)
+    ref_cache, ref_out = parity.oracle(w)
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    parity.check_output(w["dtype"], d.output_f64(), ref_out, what=spec.name)
+    return w, d, ref_cache, ref_out
+
+
+EDGES = {
+    "first_token": dict(past=[0], new=[1]),
+    "window0": dict(local_window_size=0),
+    "window5": dict(local_window_size=5, past=[40, 3], new=[9, 30]),
+    "no_rotary": dict(do_rotary=0),
+    "interleaved": dict(rotary_interleaved=1),
+    "bs32": dict(block_size=32),
+    "bs128": dict(block_size=128, past=[200, 3], new=[2, 140]),
+    "bs256": dict(block_size=256, past=[300], new=[20]),
+    "one_head": dict(num_heads=1),
+    "three_heads": dict(num_heads=3, past=[9, 0], new=[12, 23]),
+    "softcap": dict(softcap=0.5, dtype="f16"),
+    "f16": dict(dtype="f16"),
+    "v_not_mult4": dict(v_head_size=30),
+    "v_eq_hs": dict(v_head_size=64, scale=1 / 8),
+    "hs80_padded": dict(head_size=80, v_head_size=48, rotary_offset=16, rotary_dim=64),
+    "glm_dims_128heads": dict(num_heads=128, head_size=192, v_head_size=128, rotary_dim=64,
+                              rotary_offset=128, block_size=64, past=[100, 700], new=[1, 1]),
+    "dsv3_dims_multi_token": dict(num_heads=16, head_size=576, v_head_size=512, rotary_dim=64,
+                                  rotary_offset=512, block_size=16, past=[33, 0], new=[9, 17]),
+    "empty_middle_seq": dict(past=[4, 50, 7], new=[3, 0, 5]),
+    "long_context": dict(past=[20000], new=[1], block_size=64),
+    "slot_drop": dict(slot_drop_frac=0.3, past=[10, 20], new=[20, 10]),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGES))
+def test_edge_case(name):
+    _edge(_spec(name=name, **EDGES[name]))
+
+
+def test_first_token_and_window0_exact():
+    """A token that sees only itself outputs its own value row, bit for bit."""
+    torch = _torch()
+    for kw in (dict(past=[0], new=[1]), dict(local_window_size=0)):
+        w, d, ref_cache, _ = _edge(_spec(name="exact", **kw))
+        hs, vhs, H = 64, 32, 4
+        got = d.output.view(torch.int16).cpu().numpy().view(np.uint16)
+        flat = ref_cache.reshape(-1, hs)
+        for t in range(w["dims"]["token_count"]):
+            s = w["slot_mapping"][t]
+            for h in range(H):
+                assert np.array_equal(got[t, h * vhs:(h + 1) * vhs], flat[s, :vhs])
+
+
+def test_zero_tokens_no_launch():
+    torch = _torch()
+    w = wl.build(_spec(name="zero", past=[5], new=[1]))
+    w["dims"]["token_count"] = 0
+    d = _dev(w, workspace=False)
+    assert d.write() == 0
+    assert d.attention() == 0
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small():
+    _torch()
+    from paged_absorbed_mla_amd import _lib
+    w = wl.make("c1")
+    d = _dev(w)
+    st = _lib.pa_latent_attention(d.attrs, d.dims, d.code, d.query, d.key_cache, d.cos, d.sin, d.cumseq,
+                                  d.past, d.block_table, d.output, d.workspace, d.ws_bytes - 256,
+                                  check=False)
+    assert st == _lib.PA_ERR_WORKSPACE_TOO_SMALL
