@@ -1,4 +1,5 @@
-// Attention instance: f16 storage, head sizes padded to 192/128, 4 waves, 64-key tiles.
+// Attention instance: f16 storage, head sizes padded to 192/128, 4 waves, 64-key tiles,
+// query channels [0, 192) held in registers.
 #include "../pa_attn.cuh"
 
-PA_DEFINE_ATTN_INSTANCE(F16, f16, 192, 128, 4, 64)
+PA_DEFINE_ATTN_INSTANCE(F16, f16, 192, 128, 4, 64, 192)

@@ -122,19 +122,20 @@ __device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
 
 // State one wavefront carries across the KV tiles of a piece: its 32 query
 // rows as MFMA B fragments, and the transposed output accumulators.
-template <typename DT, int HSP, int VHSP, int KT>
+template <typename DT, int HSP, int VHSP, int KT, int QREG>
 struct WaveState {
-  static constexpr int NKK = HSP / 16;
+  static constexpr int NKR = QREG / 16;
   static constexpr int NMT = VHSP / 32;
-  u32x4_t qf[NKK];
+  u32x4_t qf[NKR];
   f32x16_t o[NMT];
   float m_run, l_run;
 };
 
 // S^T = K Q^T for one LDS tile, softmax update, O^T += V^T P^T.
-template <typename DT, int HSP, int VHSP, int KT>
-__device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT>& st, const uint8_t* L, int key0,
-                                             int pos, int lo_row, bool softcap_on, const AttnParams& p) {
+template <typename DT, int HSP, int VHSP, int KT, int QREG>
+__device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>& st, const uint8_t* L,
+                                             const uint16_t* qrest, int key0, int pos, int lo_row,
+                                             bool softcap_on, const AttnParams& p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;
   constexpr int NKK = HSP / 16;
@@ -150,16 +151,42 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT>& st, c
   const uint8_t* qb[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) qb[r] = L + l32 * CPR * 16 + (((2 * r + hi) ^ swq) << 4);
+  // Software pipeline: the A fragment of step n is read QPF steps ahead; the
+  // scheduling fences keep the compiler from hoisting all reads at once.
+  // Channels [0, QREG) of the query come from registers, [QREG, HSP) from the
+  // wave's persistent LDS rows (row l32, stride QRS elements).
+  constexpr int NKR = QREG / 16;
+  constexpr int QRS = HSP - QREG + 8;
+  constexpr int QPF = 4;
+  constexpr int QSTEPS = NSUB * NKK;
   f32x16_t s[NSUB];
 #pragma unroll
-  for (int sub = 0; sub < NSUB; ++sub) {
-    f32x16_t acc = f32x16_t{};
+  for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x16_t{};
+  const uint16_t* qrow_lds = qrest + l32 * QRS + 8 * hi;
+  auto qk_frag = [&](int n) -> u32x4_t {
+    const int sub = n / NKK, kk = n % NKK;
+    return *(const u32x4_t*)(qb[kk & 3] + sub * 32 * CPR * 16 + (kk >> 2) * 128);
+  };
+  auto q_frag = [&](int n) -> u32x4_t {
+    const int kk = n % NKK;
+    return *(const u32x4_t*)(qrow_lds + 16 * (kk - NKR));
+  };
+  u32x4_t qa[QPF], qq[QPF];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4_t a = *(const u32x4_t*)(qb[kk & 3] + sub * 32 * CPR * 16 + (kk >> 2) * 128);
-      acc = DT::mfma32(a, st.qf[kk], acc);
+  for (int n = 0; n < QPF; ++n) {
+    qa[n] = qk_frag(n);
+    if (n % NKK >= NKR) qq[n] = q_frag(n);
+  }
+#pragma unroll
+  for (int n = 0; n < QSTEPS; ++n) {
+    const u32x4_t cur = qa[n % QPF];
+    const u32x4_t bq = (n % NKK < NKR) ? st.qf[(n % NKK) < NKR ? (n % NKK) : 0] : qq[n % QPF];
+    if (n + QPF < QSTEPS) {
+      qa[n % QPF] = qk_frag(n + QPF);
+      if ((n + QPF) % NKK >= NKR) qq[n % QPF] = q_frag(n + QPF);
     }
-    s[sub] = acc;
+    s[n / NKK] = DT::mfma32(cur, bq, s[n / NKK]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Scale (and softcap) into log2 units, mask, tile max. Lane holds keys
   // hi*4 + (e&3) + 8*(e>>2) (+32 sub) of its row l32.
@@ -232,27 +259,32 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT>& st, c
     vb[0][par] = L + k0b * CPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
     vb[1][par] = L + (k0b + 8) * CPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
   }
+  constexpr int VPF = 3;
+  constexpr int VSTEPS = NSUB * 2 * NMT;
+  auto pv_frag = [&](int n) -> u32x4_t {
+    const int step = n / NMT, mt = n % NMT;        // step = sub * 2 + k2
+    const int coff = step * 16 * CPR * 16 + (mt >> 1) * 128;
+    const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[0][mt & 1] + coff));
+    const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[1][mt & 1] + coff));
+    const u32x2_t d0 = __builtin_bit_cast(u32x2_t, r0);
+    const u32x2_t d1 = __builtin_bit_cast(u32x2_t, r1);
+    return u32x4_t{d0[0], d0[1], d1[0], d1[1]};
+  };
+  u32x4_t va[VPF];
 #pragma unroll
-  for (int sub = 0; sub < NSUB; ++sub) {
+  for (int n = 0; n < VPF; ++n) va[n] = pv_frag(n);
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int roff = (sub * 32 + k2 * 16) * CPR * 16;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int coff = roff + (mt >> 1) * 128;
-        const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[0][mt & 1] + coff));
-        const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[1][mt & 1] + coff));
-        const u32x2_t d0 = __builtin_bit_cast(u32x2_t, r0);
-        const u32x2_t d1 = __builtin_bit_cast(u32x2_t, r1);
-        const u32x4_t a = {d0[0], d0[1], d1[0], d1[1]};
-        st.o[mt] = DT::mfma32(a, pf[sub][k2], st.o[mt]);
-      }
-    }
+  for (int n = 0; n < VSTEPS; ++n) {
+    const u32x4_t cur = va[n % VPF];
+    if (n + VPF < VSTEPS) va[n % VPF] = pv_frag(n + VPF);
+    const int step = n / NMT;
+    st.o[n % NMT] = DT::mfma32(cur, pf[step >> 1][step & 1], st.o[n % NMT]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename DT, int HSP, int VHSP, int NW, int KT>
+template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void attn_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;          // 16-byte chunks per LDS row
@@ -265,14 +297,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   constexpr int NBLK = KT / 16;         // most blocks a tile can touch (block_size >= 16)
   static_assert(HSP % 64 == 0 && VHSP % 32 == 0 && VHSP <= HSP, "head sizes");
   static_assert(KT % 32 == 0 && TILE_CHUNKS % NT == 0, "tile shape");
-  constexpr int QSTRIDE = HSP + 8;      // staged query row, padded by 16 bytes against bank conflicts
+  static_assert(QREG % 16 == 0 && QREG <= HSP, "register part of the query");
+  // LDS: [KV tile buffers | persistent query rows, channels >= QREG]. Before the
+  // tile loop the buffer region stages the register part of the query.
+  constexpr int QSTRIDE = QREG + 8;     // staged rows padded by 16 bytes against bank conflicts
+  constexpr int QRS = HSP - QREG + 8;
   constexpr int BUF_BYTES = TILE_CHUNKS * 16;
-  constexpr int Q_BYTES = NW * 32 * QSTRIDE * 2;
-  constexpr int LDS_BYTES = (2 * BUF_BYTES > Q_BYTES) ? 2 * BUF_BYTES : Q_BYTES;
+  constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
+  constexpr int KV_BYTES = (2 * BUF_BYTES > QSTAGE_BYTES) ? 2 * BUF_BYTES : QSTAGE_BYTES;
+  constexpr int QREST_BYTES = (QREG < HSP) ? RW * QRS * 2 : 0;
+  constexpr int LDS_BYTES = KV_BYTES + QREST_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
 
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // wave index, scalar
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -325,12 +364,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     const bool wave_active = w * 32 < t.nrows;
     const int64_t qrow = (int64_t)(cum_b + tq) * p.H + h;
 
-    WaveState<DT, HSP, VHSP, KT> st;
+    WaveState<DT, HSP, VHSP, KT, QREG> st;
     // Query rows of this wave, staged through LDS (free between pieces),
     // RoPE'd there with one thread per rotary pair, read back as fragments
     // (row l32, channels 16 kk + 8 hi .. + 8).
+    uint16_t* const qrest = (uint16_t*)(lds_raw + KV_BYTES) + w * 32 * QRS;
     {
       uint16_t* qs = (uint16_t*)lds_raw + w * 32 * QSTRIDE;
+      // element (r, c) of this wave's staged query rows
+      auto qel = [&](int r, int c) -> uint16_t* { return c < QREG ? qs + r * QSTRIDE + c : qrest + r * QRS + (c - QREG); };
       constexpr int QCH = HSP / 8;
       for (int idx = lane; idx < 32 * QCH; idx += 64) {
         const int r = idx / QCH;
@@ -343,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           const int64_t gq = (int64_t)(cum_b + tr) * p.H + (Rr - tr * p.H);
           v = *(const u32x4_t*)(p.query + gq * p.hs + c0);
         }
-        *(u32x4_t*)(qs + r * QSTRIDE + c0) = v;
+        *(u32x4_t*)qel(r, c0) = v;
       }
       __syncthreads();
       if (p.do_rotary) {
@@ -358,15 +400,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           const int d2 = p.interleaved ? d1 + 1 : d1 + half;
           const float c = DT::to_f32(p.cos_t[(int64_t)posr * half + k]);
           const float sn = DT::to_f32(p.sin_t[(int64_t)posr * half + k]);
-          const float x1 = DT::to_f32(qs[r * QSTRIDE + d1]);
-          const float x2 = DT::to_f32(qs[r * QSTRIDE + d2]);
-          qs[r * QSTRIDE + d1] = (uint16_t)DT::from_f32(x1 * c - x2 * sn);
-          qs[r * QSTRIDE + d2] = (uint16_t)DT::from_f32(x2 * c + x1 * sn);
+          uint16_t* e1 = qel(r, d1);
+          uint16_t* e2 = qel(r, d2);
+          const float x1 = DT::to_f32(*e1);
+          const float x2 = DT::to_f32(*e2);
+          *e1 = (uint16_t)DT::from_f32(x1 * c - x2 * sn);
+          *e2 = (uint16_t)DT::from_f32(x2 * c + x1 * sn);
         }
       }
       __syncthreads();
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+      for (int kk = 0; kk < QREG / 16; ++kk)
         st.qf[kk] = *(const u32x4_t*)(qs + l32 * QSTRIDE + 16 * kk + 8 * hi);
       __syncthreads();
     }
@@ -388,28 +432,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
       int blks[NBLK];
 #pragma unroll
       for (int e = 0; e < NBLK; ++e) blks[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
-      const bool interior = key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP;
       uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
+      if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP) {
+        // Interior tile: every slot is a real cache chunk.
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
-        const int kfirst = ((it * NW + w) * 64) / CPR;        // wave-uniform first key of the slots
-        const int e = kfirst >> p.bs_log2;
-        int blk = blks[0];
+        for (int it = 0; it < LOADS; ++it) {
+          const int e = (((it * NW + w) * 64) / CPR) >> p.bs_log2;   // scalar: the slots' block
+          int blk = blks[0];
 #pragma unroll
-        for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
-        const uint16_t* base = p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.hs;
-        uint8_t* dst = dst0 + it * NT * 16;
-        if (interior) {
-          __builtin_amdgcn_global_load_lds((const uint8_t*)base + load_off[it], dst, 16, 0, 0);
-        } else {
+          for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
+          const uint8_t* base = (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.hs);
+          __builtin_amdgcn_global_load_lds(base + load_off[it], dst0 + it * NT * 16, 16, 0, 0);
+        }
+      } else {
+        // Boundary tile: keys outside [kv_lo, kv_hi) or channels >= hs are zero-filled.
+#pragma unroll 1
+        for (int it = 0; it < LOADS; ++it) {
           const int pidx = it * NT + (int)threadIdx.x;
           const int k = pidx / CPR;
           const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
           const int j = key0 + k;
-          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs)
-            __builtin_amdgcn_global_load_lds((const uint8_t*)base + load_off[it], dst, 16, 0, 0);
-          else
+          uint8_t* dst = dst0 + it * NT * 16;
+          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs) {
+            const int blkv = p.bt[(int64_t)b * p.MB + (j >> p.bs_log2)];
+            const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
+            __builtin_amdgcn_global_load_lds(p.cache + row * p.hs + lc * 8, dst, 16, 0, 0);
+          } else {
             *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+          }
         }
       }
     };
@@ -421,7 +471,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
-        tile_compute<DT, HSP, VHSP, KT>(st, lds_raw + bufi * BUF_BYTES, tt * KT, pos, lo_row, softcap_on, p);
+        tile_compute<DT, HSP, VHSP, KT, QREG>(st, lds_raw + bufi * BUF_BYTES, qrest, tt * KT, pos, lo_row,
+                                              softcap_on, p);
       }
     } else {
       for (int tt = tile_a; tt < tile_b; ++tt) {
@@ -438,23 +489,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
       if (row_ok) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         uint16_t* orow = p.out + qrow * p.vhs;
-        const bool vec_ok = (p.vhs & 3) == 0;
+        if (p.vhs == VHSP) {
+          // Lane writes channels mt*32 + hi*4 + 8*grp .. + 3 of its row: one base
+          // address, immediate offsets.
+          uint16_t* ob = orow + hi * 4;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
+          for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const int c0 = mt * 32 + hi * 4 + 8 * grp;
-            const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
-            const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
-            const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
-            const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
-            if (vec_ok) {
-              if (c0 < p.vhs) *(u32x2_t*)(orow + c0) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-            } else {
-              if (c0 + 0 < p.vhs) orow[c0 + 0] = (uint16_t)e0;
-              if (c0 + 1 < p.vhs) orow[c0 + 1] = (uint16_t)e1;
-              if (c0 + 2 < p.vhs) orow[c0 + 2] = (uint16_t)e2;
-              if (c0 + 3 < p.vhs) orow[c0 + 3] = (uint16_t)e3;
+            for (int grp = 0; grp < 4; ++grp) {
+              const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
+              const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
+              const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
+              const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
+              *(u32x2_t*)(ob + mt * 32 + 8 * grp) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+            }
+          }
+        } else {
+          for (int mt = 0; mt < NMT; ++mt) {
+            for (int e = 0; e < 16; ++e) {
+              const int c = mt * 32 + hi * 4 + 8 * (e >> 2) + (e & 3);
+              if (c < p.vhs) orow[c] = (uint16_t)DT::from_f32(st.o[mt][e] * inv);
             }
           }
         }
@@ -486,18 +540,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 // Merge the partials of every query tile that several workgroups processed:
 // with M = max_i m_i (log2 domain) and w_i = 2^(m_i - M),
 // out = sum_i w_i acc_i / sum_i w_i l_i, rounded to nearest even.
+// Grid: (query tiles, rows / kCombineRows); one thread per 4 output channels.
+constexpr int kCombineRows = 16;
+
 template <typename DT, int VHSP, int RW>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int i = blockIdx.x;
-  if (i >= p.header[1]) return;
-  const MTile t = p.mt[i];
+  if (i >= ld_uniform(p.header + 1)) return;
+  const MTile t = ld_uniform_tile(p.mt + i);
   if (t.npieces <= 1) return;
   constexpr int C4 = VHSP / 4;
-  const int cum_b = p.cumseq[t.b];
-  for (int idx = threadIdx.x; idx < t.nrows * C4; idx += 256) {
-    const int r = idx / C4;
-    const int c0 = (idx - r * C4) * 4;
-    if (c0 >= p.vhs) continue;
+  const int cum_b = ld_uniform(p.cumseq + t.b);
+  const int r0 = blockIdx.y * kCombineRows;
+  for (int idx = threadIdx.x; idx < kCombineRows * C4; idx += 256) {
+    const int r = r0 + idx / C4;
+    const int c0 = (idx % C4) * 4;
+    if (r >= t.nrows || c0 >= p.vhs) continue;
     float mx = -INFINITY;
     for (int q = 0; q < t.npieces; ++q)
       mx = fmaxf(mx, p.part_ml[((int64_t)(t.part_base + q) * RW + r) * 2]);
@@ -516,9 +574,15 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     const int tq = R / p.H;
     const int h = R - tq * p.H;
     uint16_t* orow = p.out + ((int64_t)(cum_b + tq) * p.H + h) * p.vhs;
+    if ((p.vhs & 3) == 0) {
+      const uint32_t e0 = DT::from_f32(acc[0] * inv), e1 = DT::from_f32(acc[1] * inv);
+      const uint32_t e2 = DT::from_f32(acc[2] * inv), e3 = DT::from_f32(acc[3] * inv);
+      *(u32x2_t*)(orow + c0) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (c0 + k < p.vhs) orow[c0 + k] = (uint16_t)DT::from_f32(acc[k] * inv);
+      for (int k = 0; k < 4; ++k)
+        if (c0 + k < p.vhs) orow[c0 + k] = (uint16_t)DT::from_f32(acc[k] * inv);
+    }
   }
 }
 
@@ -528,18 +592,18 @@ typedef hipError_t (*AttnOccFn)(int*);
 }  // namespace pa
 
 #define PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, SUF) attn_##DTN##_##HSP##_##VHSP##_##NW##_##KT##_##SUF
-#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT)                                                 \
+#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT, QREG)                                               \
   namespace pa {                                                                                            \
   hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                              \
-    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT>;                                            \
+    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG>;                                            \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0);  \
   }                                                                                                         \
   hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,         \
                                                         int cgrid, hipStream_t s) {                           \
-    attn_kernel<DT, HSP, VHSP, NW, KT><<<grid, NW * 64, 0, s>>>(p);                                         \
+    attn_kernel<DT, HSP, VHSP, NW, KT, QREG><<<grid, NW * 64, 0, s>>>(p);                                         \
     hipError_t e = hipGetLastError();                                                                       \
     if (e != hipSuccess || !combine) return e;                                                              \
-    combine_kernel<DT, VHSP, NW * 32><<<cgrid, 256, 0, s>>>(p);                                              \
+    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);                                              \
     return hipGetLastError();                                                                               \
   }                                                                                                         \
   }

@@ -7,7 +7,7 @@
 // (docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs", module
 // comment "Capture safety": geometry fixed by tensor shapes, positions and
 // blocks resolved on device).
-#include "pa_attn.cuh"
+#include "pa_attn16.cuh"
 
 #include <algorithm>
 #include <mutex>
@@ -166,10 +166,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 // Instance table
 // ---------------------------------------------------------------------------
 
-PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 4, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 4, 64)
-PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 1, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 16, 64)
+PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 16, 64)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 1, 64)
@@ -190,8 +188,7 @@ struct InstanceEntry {
    &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)}
 
 static const InstanceEntry kInstances[] = {
-    PA_ENTRY(16, bf16, 576, 512, 4, 64), PA_ENTRY(10, f16, 576, 512, 4, 64),
-    PA_ENTRY(16, bf16, 576, 512, 1, 64), PA_ENTRY(10, f16, 576, 512, 1, 64),
+    PA_ENTRY(16, bf16, 576, 512, 16, 64), PA_ENTRY(10, f16, 576, 512, 16, 64),
     PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
     PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
     PA_ENTRY(16, bf16, 64, 32, 1, 32),   PA_ENTRY(10, f16, 64, 32, 1, 32),
@@ -200,19 +197,20 @@ static const InstanceEntry kInstances[] = {
 
 static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
   for (const auto& e : kInstances)
-    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.nw && e.kt == c.kt) return &e;
+    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.id_nw() && e.kt == c.kt) return &e;
   return nullptr;
 }
 
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
+  cfg->paired = 0;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 64; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 64; cfg->paired = 1; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
-  cfg->nw = rows_per_seq >= 96 ? 4 : 1;
+  cfg->nw = cfg->paired ? 4 : (rows_per_seq >= 96 ? 4 : 1);
   if (cfg->hsp == 64 && cfg->nw == 4) cfg->kt = 64;   // staged query rows need 2 tiles >= 32 * nw rows
   return find_instance(g.dtype, *cfg) != nullptr;
 }
@@ -220,7 +218,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
 hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, int* blocks_per_cu) {
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int, int, int>, int> cache;
-  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.nw, cfg.kt);
+  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.id_nw(), cfg.kt);
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
@@ -245,12 +243,21 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   const int RW = cfg.rows();
   L.max_mtiles = (g.T * g.H + RW - 1) / RW + std::min<int64_t>(g.B, g.T);
   const int64_t g_split = (int64_t)num_cus * blocks_per_cu;
-  L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
-  L.part_cap = split_kv ? L.max_mtiles + L.grid : 0;
+  if (cfg.paired) {
+    // Workgroups i and i + 8 (mod 16) share a range: the grid is a multiple of 16.
+    const int64_t ranges = split_kv ? std::max<int64_t>(8, (g_split / 16) * 8)
+                                    : ((std::max<int64_t>(L.max_mtiles, 1) + 7) / 8) * 8;
+    L.ranges = (int)ranges;
+    L.grid = (int)(2 * ranges);
+  } else {
+    L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
+    L.ranges = L.grid;
+  }
+  L.part_cap = split_kv ? L.max_mtiles + L.ranges : 0;
   size_t off = 0;
   L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
   L.off_zero = off; off = align256(off + 16);
-  L.off_wg_range = off; off = align256(off + (size_t)(L.grid + 1) * sizeof(int32_t));
+  L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
   L.off_seq_base = off; off = align256(off + (size_t)(g.B + 1) * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
@@ -275,7 +282,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.RW = cfg.rows();
   sp.KT = cfg.kt;
   sp.window = g.window;
-  sp.grid = ws.grid;
+  sp.grid = ws.ranges;
   sp.split_kv = split_kv ? 1 : 0;
   sp.max_mtiles = ws.max_mtiles;
   sp.part_cap = ws.part_cap;
