@@ -48,7 +48,22 @@ def parse():
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """A plain copy of known size: reads and writes exactly mib MiB, so the HBM
+    byte counters of its dispatch give the scale factor of those counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "reads": n, "writes": n}), flush=True)
 
 
 def cpu_baseline(w, target_s: float):
@@ -90,6 +105,9 @@ def cpu_baseline(w, target_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is single-device; "
               "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)

@@ -42,6 +42,8 @@
 //     combine kernel with a log-sum-exp weighting.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -87,6 +89,48 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ int lds_swizzle(int key) { return (key & 7) ^ ((key >> 3) & 1); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ds_read_b64_tr_b16 at LDS address addr + OFF, issued without compiler
+// dependency tracking: the caller waits (lgkm_wait_n) before using the result.
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16_b64_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  u32x2_t d;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+  return d;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// s_waitcnt vmcnt(ahead * PER) for a runtime ahead in [0, MAXA] (the count is an
+// immediate, so each value gets its own instruction).
+template <int PER, int MAXA>
+__device__ __forceinline__ void vm_wait_tiles(int ahead) {
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); return; }
+  }
+  if constexpr (MAXA >= 1) {
+    if (ahead >= 1) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); return; }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // softcap * tanh(scale * s / softcap), returned in log2 units (times log2 e).
 // tanh(z) = 1 - 2 / (e^{2z} + 1): saturates to +-1 for large |z| (e^{2z} = inf

@@ -49,13 +49,16 @@ __device__ __forceinline__ void tile_compute16(WaveState16<DT, HSP, VHSP, KT>& s
   const uint8_t* kb[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) kb[r] = L + l16 * CPR * 16 + (((4 * r + q4) ^ swk) << 4);
-  constexpr int QPF = 4;
+  // Step n: channel step kk = n / NSUB, accumulator sub = n % NSUB; even and
+  // odd channel steps go to separate accumulators (summed afterwards), so at
+  // least four independent MFMA chains interleave.
+  constexpr int QPF = 8;
   constexpr int QSTEPS = NSUB * NKK;
-  f32x4_t s[NSUB];
+  f32x4_t s[NSUB], s2[NSUB];
 #pragma unroll
-  for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int sub = 0; sub < NSUB; ++sub) { s[sub] = f32x4_t{0.f, 0.f, 0.f, 0.f}; s2[sub] = s[sub]; }
   auto k_frag = [&](int n) -> u32x4_t {
-    const int sub = n / NKK, kk = n % NKK;
+    const int kk = n / NSUB, sub = n % NSUB;
     return *(const u32x4_t*)(kb[kk & 1] + sub * 16 * CPR * 16 + (kk >> 1) * 128);
   };
   u32x4_t ka[QPF];
@@ -65,9 +68,13 @@ __device__ __forceinline__ void tile_compute16(WaveState16<DT, HSP, VHSP, KT>& s
   for (int n = 0; n < QSTEPS; ++n) {
     const u32x4_t cur = ka[n % QPF];
     if (n + QPF < QSTEPS) ka[n % QPF] = k_frag(n + QPF);
-    s[n / NKK] = DT::mfma16(cur, st.qf[n % NKK], s[n / NKK]);
+    const int kk = n / NSUB, sub = n % NSUB;
+    if (kk & 1) s2[sub] = DT::mfma16(cur, st.qf[kk], s2[sub]);
+    else s[sub] = DT::mfma16(cur, st.qf[kk], s[sub]);
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) s[sub] += s2[sub];
 
   // Lane holds keys 16 sub + 4 q4 + i of its row l16.
   if (softcap_on) {
@@ -123,39 +130,50 @@ __device__ __forceinline__ void tile_compute16(WaveState16<DT, HSP, VHSP, KT>& s
   const int cq = lane & 3;
   const int kr = 4 * q4 + jj;              // key within a 16-key half, < 16
   const int swv = lds_swizzle(kr);         // same for kr + 16 (period 16)
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const uint8_t* vb[4];
+  // The transposing reads are issued through inline asm: the compiler treats
+  // the intrinsic as aliasing every in-flight global->LDS copy and would wait
+  // for the next tile's copy before each of them. Their completion is tracked
+  // here instead: step n's two reads are followed by at most 2 * (VPF - 1)
+  // newer LDS operations when step n is consumed (no scalar loads are in
+  // flight in this loop), so lgkmcnt(2 * (VPF - 1)) orders them.
+  uint32_t vb[4];
 #pragma unroll
   for (int m4 = 0; m4 < 4; ++m4)
-    vb[m4] = L + kr * CPR * 16 + (((2 * m4 + (cq >> 1)) ^ swv) << 4) + (cq & 1) * 8;
-  constexpr int VPF = 4;
+    vb[m4] = lds_addr(L + kr * CPR * 16 + (((2 * m4 + (cq >> 1)) ^ swv) << 4) + (cq & 1) * 8);
+  constexpr int VPF = 8;
   constexpr int VSTEPS = NKS * NMT;
-  auto v_frag = [&](int n) -> u32x4_t {
-    const int ks = n / NMT, mt = n % NMT;
-    const int off = ks * 32 * CPR * 16 + (mt >> 2) * 128;
-    const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[mt & 3] + off));
-    const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[mt & 3] + off + 16 * CPR * 16));
-    const u32x2_t d0 = __builtin_bit_cast(u32x2_t, r0);
-    const u32x2_t d1 = __builtin_bit_cast(u32x2_t, r1);
-    return u32x4_t{d0[0], d0[1], d1[0], d1[1]};
-  };
+  static_assert(2 * (VPF - 1) <= 15, "lgkmcnt range");
+  constexpr int ROW16 = 16 * CPR * 16;
+  static_assert(ROW16 + (NKS - 1) * 32 * CPR * 16 + (NMT / 4 - 1) * 128 < 65536, "ds offset range");
+  lgkm_wait_n<0>();   // no scalar load may be in flight while lgkmcnt counts LDS reads
   u32x4_t va[VPF];
-#pragma unroll
-  for (int n = 0; n < VPF; ++n) va[n] = v_frag(n);
-#pragma unroll
-  for (int n = 0; n < VSTEPS; ++n) {
-    const u32x4_t cur = va[n % VPF];
-    if (n + VPF < VSTEPS) va[n % VPF] = v_frag(n + VPF);
-    st.o[n % NMT] = DT::mfma16(cur, pf[n / NMT], st.o[n % NMT]);
+  auto v_issue = [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    constexpr int ks = n / NMT, mt = n % NMT;
+    constexpr int off = ks * 32 * CPR * 16 + (mt >> 2) * 128;
+    const u32x2_t r0 = ds_read_tr16_b64_asm<off>(vb[mt & 3]);
+    const u32x2_t r1 = ds_read_tr16_b64_asm<off + ROW16>(vb[mt & 3]);
+    va[n % VPF] = u32x4_t{r0[0], r0[1], r1[0], r1[1]};
+  };
+  static_for<0, VPF>(v_issue);
+  static_for<0, VSTEPS>([&](auto N) {
+    constexpr int n = decltype(N)::value;
+    constexpr int left = VSTEPS - 1 - n;
+    lgkm_wait_n<2 * (left < VPF - 1 ? left : VPF - 1)>();
     __builtin_amdgcn_sched_barrier(0);
-  }
+    st.o[n % NMT] = DT::mfma16(va[n % VPF], pf[n / NMT], st.o[n % NMT]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (n + VPF < VSTEPS) v_issue(std::integral_constant<int, n + VPF>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 // Workgroup i handles rows [64 h, 64 h + 64) of every query tile in unit range
 // k, with h = (i >> 3) & 1 and k = (i >> 4) * 8 + (i & 7): the pair (i, i + 8)
-// lands on one XCD. The schedule's ranges are indexed by k.
-template <typename DT, int HSP, int VHSP, int KT>
+// lands on one XCD. The schedule's ranges are indexed by k. NBUF LDS tile
+// buffers keep up to NBUF - 1 tiles of copies in flight per workgroup.
+template <typename DT, int HSP, int VHSP, int KT, int NBUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void attn16_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4;
@@ -167,12 +185,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void a
   constexpr int NMT = VHSP / 16;
   constexpr int RW = 128;              // rows of a query tile (both halves)
   constexpr int HALF = 64;
-  constexpr int NBLK = KT / 16;
   static_assert(HSP % 64 == 0 && VHSP % 16 == 0 && VHSP <= HSP && KT % 32 == 0 && TILE_CHUNKS % NT == 0, "shape");
   constexpr int QSTRIDE = HSP + 8;
   constexpr int BUF_BYTES = TILE_CHUNKS * 16;
   constexpr int QSTAGE_BYTES = HALF * QSTRIDE * 2;
-  constexpr int LDS_BYTES = (2 * BUF_BYTES > QSTAGE_BYTES) ? 2 * BUF_BYTES : QSTAGE_BYTES;
+  constexpr int LDS_BYTES = (NBUF * BUF_BYTES > QSTAGE_BYTES) ? NBUF * BUF_BYTES : QSTAGE_BYTES;
+  static_assert(NBUF >= 2 && (NBUF - 2) * (KT * CPR / (4 * 64)) <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
 
@@ -196,13 +214,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void a
     i = lo;
   }
   const bool softcap_on = p.softcap > 0.0f;
+  // Wave w copies LDS slots [w * LOADS * 64, (w + 1) * LOADS * 64): keys
+  // [w * KW, (w + 1) * KW) of the tile, KW = KT / NW <= 16 keys, which always lie
+  // in one cache block (block_size >= 16, a power of two). Byte offset of each lane's chunk
+  // relative to the first of those keys' rows (tile-independent).
+  constexpr int KW = KT / NW;
+  static_assert(KW * CPR == LOADS * 64 && KW <= 16, "one block slice per wave (block_size >= 16)");
   int load_off[LOADS];
 #pragma unroll
   for (int it = 0; it < LOADS; ++it) {
-    const int pidx = it * NT + (int)threadIdx.x;
-    const int k = pidx / CPR;
-    const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-    load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.hs + lc * 8) * 2;
+    const int sl = it * 64 + lane;            // slot within the wave's slice
+    const int k = sl / CPR;                   // key within the slice
+    const int lc = (sl - k * CPR) ^ lds_swizzle(w * KW + k);
+    load_off[it] = (k * p.hs + lc * 8) * 2;
   }
 
   while (u < u_end) {
@@ -276,59 +300,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void a
     st.m_run = -INFINITY;
     st.l_run = 0.0f;
 
-    auto issue = [&](int tile, int bufi) {
+    // Every call issues exactly LOADS copy instructions per wave (the pipeline
+    // below counts them with vmcnt); slots of keys outside [kv_lo, kv_hi) or of
+    // channels >= hs copy 16 zero bytes from the workspace's zero page.
+    // Block-table entry of this wave's slice of `tile` (scalar load).
+    auto slice_block = [&](int tile) -> int {
+      return ld_uniform(p.bt + (int64_t)b * p.MB + min((tile * KT + w * KW) >> p.bs_log2, p.MB - 1));
+    };
+    auto issue = [&](int tile, int bufi, int blk) {
       const int key0 = tile * KT;
-      const int blk0 = key0 >> p.bs_log2;
-      const int in_blk = key0 & ((1 << p.bs_log2) - 1);
-      int blks[NBLK];
+      const int kw0 = key0 + w * KW;                       // first key of this wave's slice
+      uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * LOADS * 64 * 16;
+      const uint8_t* base = (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) +
+                                                        (kw0 & ((1 << p.bs_log2) - 1))) * p.hs);
+      if (kw0 >= t.kv_lo && kw0 + KW <= t.kv_hi && p.hs == HSP) {
 #pragma unroll
-      for (int e = 0; e < NBLK; ++e) blks[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
-      uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
-      if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP) {
-#pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-          const int e = (((it * NW + w) * 64) / CPR) >> p.bs_log2;
-          int blk = blks[0];
-#pragma unroll
-          for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
-          const uint8_t* base = (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.hs);
-          __builtin_amdgcn_global_load_lds(base + load_off[it], dst0 + it * NT * 16, 16, 0, 0);
-        }
+        for (int it = 0; it < LOADS; ++it)
+          __builtin_amdgcn_global_load_lds(base + load_off[it], dst0 + it * 64 * 16, 16, 0, 0);
       } else {
-#pragma unroll 1
+#pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-          const int pidx = it * NT + (int)threadIdx.x;
-          const int k = pidx / CPR;
-          const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-          const int j = key0 + k;
-          uint8_t* dst = dst0 + it * NT * 16;
-          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs) {
-            const int blkv = p.bt[(int64_t)b * p.MB + (j >> p.bs_log2)];
-            const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
-            __builtin_amdgcn_global_load_lds(p.cache + row * p.hs + lc * 8, dst, 16, 0, 0);
-          } else {
-            *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
-          }
+          const int sl = it * 64 + lane;
+          const int k = sl / CPR;
+          const int lc = (sl - k * CPR) ^ lds_swizzle(w * KW + k);
+          const int j = kw0 + k;
+          const bool ok = j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs;
+          const uint8_t* src = ok ? base + load_off[it] : (const uint8_t*)p.zero16;
+          __builtin_amdgcn_global_load_lds(src, dst0 + it * 64 * 16, 16, 0, 0);
         }
       }
     };
 
-    issue(tile_a, 0);
-    if (wave_active) {
-      for (int tt = tile_a; tt < tile_b; ++tt) {
-        const int bufi = (tt - tile_a) & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
+    // Copies of tiles tt + 1 .. tt + NBUF - 2 stay in flight while tile tt is
+    // computed; loads complete in order, so vmcnt(ahead * LOADS) means tile tt
+    // has landed. Buffer (tt - tile_a) % NBUF is refilled with tile
+    // tt + NBUF - 1 only after the barrier that ends every wave's work on tile tt - 1.
+    // The block-table entry of the tile issued in an iteration is loaded one
+    // iteration earlier, so the scalar load's latency stays off the copy path;
+    // the lgkmcnt(0) before the transposing reads of tile_compute16 retires it.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the previous piece's stores
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (tile_a + k < tile_b) issue(tile_a + k, k, slice_block(tile_a + k));
+    int blk_next = slice_block(tile_a + NBUF - 1);
+    for (int tt = tile_a; tt < tile_b; ++tt) {
+      const int bufi = (tt - tile_a) % NBUF;
+      const int ahead = min(NBUF - 2, tile_b - 1 - tt);
+      vm_wait_tiles<LOADS, NBUF - 2>(ahead);
+      __syncthreads();
+      const int blk_cur = blk_next;
+      blk_next = slice_block(tt + NBUF);
+      if (tt + NBUF - 1 < tile_b) issue(tt + NBUF - 1, (tt + NBUF - 1 - tile_a) % NBUF, blk_cur);
+      if (wave_active)
         tile_compute16<DT, HSP, VHSP, KT>(st, lds_raw + bufi * BUF_BYTES, tt * KT, pos, lo_row, softcap_on, p);
-      }
-    } else {
-      for (int tt = tile_a; tt < tile_b; ++tt) {
-        const int bufi = (tt - tile_a) & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
-      }
     }
     __syncthreads();
 
@@ -373,15 +397,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void a
 
 }  // namespace pa
 
-#define PA_DEFINE_ATTN16_INSTANCE(DT, DTN, HSP, VHSP, KT)                                                    \
+#define PA_DEFINE_ATTN16_INSTANCE(DT, DTN, HSP, VHSP, KT, NBUF)                                                  \
   namespace pa {                                                                                            \
   hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 16, KT, occ)(int* n) {                                              \
-    void (*fn)(AttnParams) = attn16_kernel<DT, HSP, VHSP, KT>;                                              \
+    void (*fn)(AttnParams) = attn16_kernel<DT, HSP, VHSP, KT, NBUF>;                                              \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), 256, 0);      \
   }                                                                                                         \
   hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 16, KT, launch)(const AttnParams& p, int grid, bool combine,         \
                                                         int cgrid, hipStream_t s) {                           \
-    attn16_kernel<DT, HSP, VHSP, KT><<<grid, 256, 0, s>>>(p);                                               \
+    attn16_kernel<DT, HSP, VHSP, KT, NBUF><<<grid, 256, 0, s>>>(p);                                               \
     hipError_t e = hipGetLastError();                                                                       \
     if (e != hipSuccess || !combine) return e;                                                              \
     combine_kernel<DT, VHSP, 128><<<dim3(cgrid, 128 / kCombineRows), 256, 0, s>>>(p);                        \
