@@ -37,7 +37,11 @@
  *     max_blocks_per_seq * block_size; block_table entries of every block a
  *     sequence uses lie in [0, num_blocks); slot_mapping entries are -1 or in
  *     [0, num_blocks * block_size), distinct, and consistent with block_table;
- *     rotary_rows > largest position. Violating them is undefined behaviour.
+ *     rotary_rows > largest position. Violating them gives unspecified
+ *     results, but no access leaves the caller's buffers: block ids are
+ *     clamped into [0, num_blocks), rotary positions into [0, rotary_rows),
+ *     slots past the cache are skipped like -1, and negative past lengths count
+ *     as 0 when the key ranges are planned.
  */
 #ifndef PA_LATENT_H
 #define PA_LATENT_H

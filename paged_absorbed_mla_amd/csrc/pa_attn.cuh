@@ -75,6 +75,8 @@ struct AttnParams {
   const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
   float* part_acc;          // [slots][rows][VHSP]
+  int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
+  int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H, hs, vhs, bs_log2, MB;
   int ro, rd, do_rotary, interleaved, window;
   float scale, scale_log2, softcap, softcap_inv;
@@ -103,6 +105,34 @@ __device__ __forceinline__ u32x2_t ds_read_tr16_b64_asm(uint32_t addr) {
   u32x2_t d;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
   return d;
+}
+
+// ds_read_b128 at LDS address addr + OFF, issued like ds_read_tr16_b64_asm.
+template <int OFF>
+__device__ __forceinline__ u32x4_t ds_read_b128_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  u32x4_t d;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+  return d;
+}
+
+// The lane index, opaque to the optimiser: values derived from it are
+// recomputed where they are used instead of being hoisted out of loops and
+// kept live (and spilled) across them.
+__device__ __forceinline__ int opaque_lane() {
+  int l = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data
+// format word of the gfx9 descriptor layout). Loads at offsets >= bytes return
+// zeros without touching memory.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
@@ -146,6 +176,12 @@ __device__ __forceinline__ float softcap_log2(float s, float scale, float cap, f
 // block_table, sequence lengths and the schedule the previous launch wrote.
 __device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
   return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
+// Block id clamped into [0, nblk): a block_table entry outside the cache (a
+// violated precondition) then reads some cache block instead of faulting.
+__device__ __forceinline__ int clamp_block(int blk, int64_t nblk) {
+  return (int)min(max((int64_t)blk, (int64_t)0), nblk - 1);
 }
 
 __device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
@@ -442,8 +478,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           const int posr = past_b + (t.row0 + rl) / p.H;
           const int d1 = p.interleaved ? p.ro + 2 * k : p.ro + k;
           const int d2 = p.interleaved ? d1 + 1 : d1 + half;
-          const float c = DT::to_f32(p.cos_t[(int64_t)posr * half + k]);
-          const float sn = DT::to_f32(p.sin_t[(int64_t)posr * half + k]);
+          const int64_t pr = min(max((int64_t)posr, (int64_t)0), p.prow - 1);
+          const float c = DT::to_f32(p.cos_t[pr * half + k]);
+          const float sn = DT::to_f32(p.sin_t[pr * half + k]);
           uint16_t* e1 = qel(r, d1);
           uint16_t* e2 = qel(r, d2);
           const float x1 = DT::to_f32(*e1);
@@ -475,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
       const int in_blk = key0 & ((1 << p.bs_log2) - 1);      // nonzero only when block_size > KT
       int blks[NBLK];
 #pragma unroll
-      for (int e = 0; e < NBLK; ++e) blks[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
+      for (int e = 0; e < NBLK; ++e) blks[e] = clamp_block(ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1)), p.nblk);
       uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
       if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP) {
         // Interior tile: every slot is a real cache chunk.

@@ -7,7 +7,7 @@
 // (docs.rs page "onnx-runtime-ep-cuda src/kernels/paged_attention.rs", module
 // comment "Capture safety": geometry fixed by tensor shapes, positions and
 // blocks resolved on device).
-#include "pa_attn16.cuh"
+#include "pa_attn.cuh"
 
 #include <algorithm>
 #include <mutex>
@@ -103,8 +103,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     const int rows = (p.cumseq[b + 1] - p.cumseq[b]) * p.H;
     const int row0 = (int)(i - p.seq_base[b]) * p.RW;
     const int nrows = min(p.RW, rows - row0);
-    const int pos0 = p.past[b] + row0 / p.H;
-    const int pos1 = p.past[b] + (row0 + nrows - 1) / p.H;
+    const int past_b = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
+    const int pos0 = past_b + row0 / p.H;
+    const int pos1 = past_b + (row0 + nrows - 1) / p.H;
     const int kv_hi = pos1 + 1;
     const int kv_lo = p.window >= 0 ? max(0, pos0 - p.window) : 0;
     MTile t;
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 // Instance table
 // ---------------------------------------------------------------------------
 
-PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 16, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 16, 64)
+PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 8, 32)
+PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 8, 32)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 1, 64)
@@ -188,7 +189,7 @@ struct InstanceEntry {
    &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)}
 
 static const InstanceEntry kInstances[] = {
-    PA_ENTRY(16, bf16, 576, 512, 16, 64), PA_ENTRY(10, f16, 576, 512, 16, 64),
+    PA_ENTRY(16, bf16, 576, 512, 8, 32),  PA_ENTRY(10, f16, 576, 512, 8, 32),
     PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
     PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
     PA_ENTRY(16, bf16, 64, 32, 1, 32),   PA_ENTRY(10, f16, 64, 32, 1, 32),
@@ -197,20 +198,20 @@ static const InstanceEntry kInstances[] = {
 
 static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
   for (const auto& e : kInstances)
-    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.id_nw() && e.kt == c.kt) return &e;
+    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.nw && e.kt == c.kt) return &e;
   return nullptr;
 }
 
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
-  cfg->paired = 0;
+  cfg->wide = 0;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 64; cfg->paired = 1; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 1; cfg->nw = 8; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
-  cfg->nw = cfg->paired ? 4 : (rows_per_seq >= 96 ? 4 : 1);
+  if (!cfg->wide) cfg->nw = rows_per_seq >= 96 ? 4 : 1;
   if (cfg->hsp == 64 && cfg->nw == 4) cfg->kt = 64;   // staged query rows need 2 tiles >= 32 * nw rows
   return find_instance(g.dtype, *cfg) != nullptr;
 }
@@ -218,7 +219,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
 hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, int* blocks_per_cu) {
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int, int, int>, int> cache;
-  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.id_nw(), cfg.kt);
+  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.nw, cfg.kt);
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
@@ -243,16 +244,8 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   const int RW = cfg.rows();
   L.max_mtiles = (g.T * g.H + RW - 1) / RW + std::min<int64_t>(g.B, g.T);
   const int64_t g_split = (int64_t)num_cus * blocks_per_cu;
-  if (cfg.paired) {
-    // Workgroups i and i + 8 (mod 16) share a range: the grid is a multiple of 16.
-    const int64_t ranges = split_kv ? std::max<int64_t>(8, (g_split / 16) * 8)
-                                    : ((std::max<int64_t>(L.max_mtiles, 1) + 7) / 8) * 8;
-    L.ranges = (int)ranges;
-    L.grid = (int)(2 * ranges);
-  } else {
-    L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
-    L.ranges = L.grid;
-  }
+  L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
+  L.ranges = L.grid;
   L.part_cap = split_kv ? L.max_mtiles + L.ranges : 0;
   size_t off = 0;
   L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
@@ -310,6 +303,8 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.zero16 = (const uint16_t*)sp.zero16;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
   ap.part_acc = (float*)(wsb + ws.off_part_acc);
+  ap.nblk = g.NB;
+  ap.prow = g.do_rotary ? g.P : 1;
   ap.H = g.H;
   ap.hs = g.hs;
   ap.vhs = g.vhs;

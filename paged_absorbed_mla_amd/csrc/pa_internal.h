@@ -28,11 +28,10 @@ hipError_t launch_write(const CallGeom& g, const void* key, const void* cos_t, c
 // Attention kernel configuration chosen for a call.
 struct AttnConfig {
   int hsp, vhsp;   // padded head sizes of the compiled instance
-  int nw;          // waves per workgroup; rows per query tile = 32 * nw (unpaired)
+  int nw;          // waves per workgroup
   int kt;          // keys per LDS tile
-  int paired;      // 1: two workgroups (16-row waves) share each 128-row query tile
-  int rows() const { return paired ? 128 : 32 * nw; }
-  int id_nw() const { return paired ? 16 : nw; }   // instance-table key
+  int wide;        // 1: attn_wide_kernel (8 waves, 128-row query tiles); 0: attn_kernel (32 rows per wave)
+  int rows() const { return wide ? 128 : 32 * nw; }
 };
 
 // Chooses the instance for a geometry; returns false when no compiled instance fits.
@@ -42,7 +41,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg);
 struct WsLayout {
   int64_t max_mtiles;   // upper bound on query tiles
   int grid;             // workgroups of the attention launch
-  int ranges;           // unit ranges of the schedule (grid, or grid / 2 when paired)
+  int ranges;           // unit ranges of the schedule (one per workgroup)
   int64_t part_cap;     // partial-result slots
   size_t off_header, off_wg_range, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
   size_t total;

@@ -19,14 +19,16 @@ __global__ __launch_bounds__(kWriteWaves * 64) void write_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ cos_t, const uint16_t* __restrict__ sin_t,
     const int32_t* __restrict__ slot_mapping, const int32_t* __restrict__ cumseq,
     const int32_t* __restrict__ past, uint16_t* __restrict__ cache, int64_t T, int hs, int ro, int rd,
-    int do_rotary, int interleaved, int B) {
+    int do_rotary, int interleaved, int B, int64_t num_slots, int64_t prow) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kWriteWaves + (threadIdx.x >> 6);
   if (t >= T) return;
   const int slot = slot_mapping[t];
-  if (slot < 0) return;
+  // -1 skips the row; so does a slot past the cache (a violated precondition).
+  if (slot < 0 || slot >= num_slots) return;
   const int b = find_seq(cumseq, B, t);
-  const int64_t pos = (int64_t)past[b] + (t - (int64_t)cumseq[b]);
+  // Position clamped into the rotary table (only a violated precondition moves it).
+  const int64_t pos = min(max((int64_t)past[b] + (t - (int64_t)cumseq[b]), (int64_t)0), prow - 1);
   const uint16_t* row = key + t * hs;
   uint16_t* dst = cache + (int64_t)slot * hs;
   const int nchunks = hs >> 3;
@@ -52,11 +54,13 @@ hipError_t launch_write(const CallGeom& g, const void* key, const void* cos_t, c
   if (g.dtype == 16)
     write_kernel<BF16><<<grid, block, 0, stream>>>((const uint16_t*)key, (const uint16_t*)cos_t,
                                                    (const uint16_t*)sin_t, slot, cumseq, past, (uint16_t*)cache,
-                                                   g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B);
+                                                   g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B,
+                                                   g.NB * g.bs, g.do_rotary ? g.P : 1);
   else
     write_kernel<F16><<<grid, block, 0, stream>>>((const uint16_t*)key, (const uint16_t*)cos_t,
                                                   (const uint16_t*)sin_t, slot, cumseq, past, (uint16_t*)cache,
-                                                  g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B);
+                                                  g.T, g.hs, g.ro, g.rd, g.do_rotary, g.interleaved, g.B,
+                                                   g.NB * g.bs, g.do_rotary ? g.P : 1);
   return hipGetLastError();
 }
 
