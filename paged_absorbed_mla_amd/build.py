@@ -29,6 +29,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Extra flags by source-file prefix. The four-wave 576/512 kernel keeps its PV
+# accumulators in AGPRs through inline assembly; its compiler-built MFMAs use
+# the VGPR form so S, P and the query stay in VGPRs.
+FILE_FLAGS = {"attnm_": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -48,7 +54,8 @@ def sources():
 def _compile(src: str, verbose: bool, extra) -> str:
     rel = os.path.relpath(src, CSRC).replace(os.sep, "_")
     obj = os.path.join(BUILD, rel[:-4] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    per_file = [f for pre, fl in FILE_FLAGS.items() if os.path.basename(src).startswith(pre) for f in fl]
+    cmd = [hipcc(), *HIPCC_FLAGS, *per_file, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,5 @@
+// Attention instance: bf16 storage, head sizes padded to 576/512, four waves of 32 query
+// rows with the query resident in registers, 32-key tiles, 4 LDS tile buffers.
+#include "../pa_attn_mla.cuh"
+
+PA_DEFINE_ATTN_MLA_INSTANCE(BF16, bf16, 576, 512)

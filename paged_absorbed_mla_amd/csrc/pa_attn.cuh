@@ -71,10 +71,12 @@ struct AttnParams {
   uint16_t* out;
   const int32_t* header;    // [0] work units U, [1] query tiles M, [2] partial slots used
   const int32_t* wg_range;  // [grid + 1] unit range of each workgroup
+  const int32_t* wg_tile;   // [grid] query tile holding each workgroup's first unit
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
   const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
   float* part_acc;          // [slots][rows][VHSP]
+  const uint16_t* qrot;     // [T * H][rd]: query rotary channels after RoPE (four-wave 576 kernel)
   int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H, hs, vhs, bs_log2, MB;
@@ -155,6 +157,16 @@ __device__ __forceinline__ void vm_wait_tiles(int ahead) {
     if (ahead >= 1) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); return; }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier that orders LDS only: the wave's own LDS operations
+// complete (lgkmcnt(0)) before it arrives. __syncthreads() would also drain
+// every outstanding global->LDS copy (its workgroup fence makes the compiler
+// emit vmcnt(0)), which serialises a multi-buffer copy pipeline; here copies
+// are awaited explicitly, per tile, with vmcnt before the barrier. The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int N>

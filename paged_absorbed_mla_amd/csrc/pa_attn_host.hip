@@ -20,9 +20,18 @@ struct SchedParams {
   const int32_t* cumseq;
   const int32_t* past;
   int B, H, RW, KT, window, grid, split_kv;
+  // Query RoPE pre-pass (blocks 1..): qrot[t * H + h][0 : rd] = RoPE of the
+  // query channels [ro, ro + rd) of (t, h), rounded to the storage type.
+  const uint16_t* query;
+  const uint16_t* cos_t;
+  const uint16_t* sin_t;
+  uint16_t* qrot;
+  int64_t T, prow;
+  int hs, ro, rd, interleaved, dtype;
   int64_t max_mtiles, part_cap;
   int32_t* header;
   int32_t* wg_range;
+  int32_t* wg_tile;
   int32_t* seq_base;
   MTile* mt;
   uint32_t* zero16;
@@ -77,7 +86,34 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
   return lo;
 }
 
+// Blocks 1.. of the schedule launch: RoPE of the query's rotary channels into
+// the workspace, one 8-channel chunk per thread (float32 math, nearest-even
+// rounding; same rotation as the write phase applies to key rows).
+template <typename DT>
+__device__ void query_rope_chunk(const SchedParams& p, int64_t idx) {
+  const int cpr = p.rd >> 3;                      // rotary chunks per row
+  const int64_t row = idx / cpr;                  // t * H + h
+  const int c0 = p.ro + (int)(idx - row * cpr) * 8;
+  const int64_t t = row / p.H;
+  const int b = find_seq(p.cumseq, p.B, t);
+  const int64_t pos = min(max((int64_t)p.past[b] + (t - (int64_t)p.cumseq[b]), (int64_t)0), p.prow - 1);
+  const uint16_t* qrow = p.query + row * p.hs;
+  float x[8];
+  unpack8<DT>(*(const u32x4_t*)(qrow + c0), x);
+  rope_chunk<DT>(x, qrow, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
+  *(u32x4_t*)(p.qrot + row * p.rd + (c0 - p.ro)) = pack8<DT>(x);
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
+  if (blockIdx.x > 0) {
+    const int64_t n = p.T * p.H * (p.rd >> 3);
+    const int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x;
+    if (idx < n) {
+      if (p.dtype == 16) query_rope_chunk<BF16>(p, idx);
+      else query_rope_chunk<F16>(p, idx);
+    }
+    return;
+  }
   if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
   // A. query tiles per sequence, prefix-summed into seq_base.
   const int64_t M_all = block_exclusive_scan(
@@ -143,12 +179,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     p.wg_range[w] = v;
   }
   __syncthreads();
-  // E. pieces per query tile.
+  // E. pieces per query tile, and the query tile holding each workgroup's
+  // first unit (the last i with mt[i].unit0 <= wg_range[w]).
   for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
     const int w0 = wg_of_unit(p.wg_range, p.grid, p.mt[i].unit0);
     const int w1 = wg_of_unit(p.wg_range, p.grid, p.mt[i + 1].unit0 - 1);
     p.mt[i].w_first = w0;
     p.mt[i].npieces = w1 - w0 + 1;
+  }
+  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
+    const int uw = p.wg_range[w];
+    int64_t lo = 0, hi = M > 0 ? M - 1 : 0;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (p.mt[mid].unit0 <= uw) lo = mid; else hi = mid - 1;
+    }
+    p.wg_tile[w] = (int32_t)lo;
   }
   __syncthreads();
   // F. partial slots for the tiles that several workgroups share.
@@ -169,6 +215,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 
 PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 8, 32)
 PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 8, 32)
+PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 4, 32)
+PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 4, 32)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 4, 64)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 1, 64)
@@ -190,6 +238,7 @@ struct InstanceEntry {
 
 static const InstanceEntry kInstances[] = {
     PA_ENTRY(16, bf16, 576, 512, 8, 32),  PA_ENTRY(10, f16, 576, 512, 8, 32),
+    PA_ENTRY(16, bf16, 576, 512, 4, 32),  PA_ENTRY(10, f16, 576, 512, 4, 32),
     PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
     PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
     PA_ENTRY(16, bf16, 64, 32, 1, 32),   PA_ENTRY(10, f16, 64, 32, 1, 32),
@@ -207,7 +256,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   cfg->wide = 0;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 1; cfg->nw = 8; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
@@ -251,10 +300,16 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
   L.off_zero = off; off = align256(off + 16);
   L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
+  L.off_wg_tile = off; off = align256(off + (size_t)L.ranges * sizeof(int32_t));
   L.off_seq_base = off; off = align256(off + (size_t)(g.B + 1) * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
   L.off_part_acc = off; off = align256(off + (size_t)L.part_cap * RW * cfg.vhsp * sizeof(float));
+  L.off_qrot = 0;
+  if (cfg.wide == 2 && g.do_rotary) {
+    L.off_qrot = off;
+    off = align256(off + (size_t)(g.T * g.H * g.rd) * 2);
+  }
   L.total = off;
   return L;
 }
@@ -281,10 +336,24 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.part_cap = ws.part_cap;
   sp.header = (int32_t*)(wsb + ws.off_header);
   sp.wg_range = (int32_t*)(wsb + ws.off_wg_range);
+  sp.wg_tile = (int32_t*)(wsb + ws.off_wg_tile);
   sp.seq_base = (int32_t*)(wsb + ws.off_seq_base);
   sp.mt = (MTile*)(wsb + ws.off_mtiles);
   sp.zero16 = (uint32_t*)(wsb + ws.off_zero);
-  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(sp);
+  sp.query = (const uint16_t*)query;
+  sp.cos_t = (const uint16_t*)cos_t;
+  sp.sin_t = (const uint16_t*)sin_t;
+  sp.qrot = ws.off_qrot ? (uint16_t*)(wsb + ws.off_qrot) : nullptr;
+  sp.T = g.T;
+  sp.prow = g.do_rotary ? g.P : 1;
+  sp.hs = g.hs;
+  sp.ro = g.ro;
+  sp.rd = g.rd;
+  sp.interleaved = g.interleaved;
+  sp.dtype = g.dtype;
+  const int64_t rope_chunks = sp.qrot ? g.T * g.H * (g.rd >> 3) : 0;
+  const int64_t rope_blocks = (rope_chunks + kSchedThreads - 1) / kSchedThreads;
+  schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -299,10 +368,12 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.out = (uint16_t*)out;
   ap.header = sp.header;
   ap.wg_range = sp.wg_range;
+  ap.wg_tile = sp.wg_tile;
   ap.mt = sp.mt;
   ap.zero16 = (const uint16_t*)sp.zero16;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
   ap.part_acc = (float*)(wsb + ws.off_part_acc);
+  ap.qrot = sp.qrot;
   ap.nblk = g.NB;
   ap.prow = g.do_rotary ? g.P : 1;
   ap.H = g.H;

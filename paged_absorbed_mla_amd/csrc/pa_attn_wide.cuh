@@ -245,7 +245,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
       const uint32_t boff = (uint32_t)(bufi * BUF_BYTES);
       const int ahead = min(NB - 2, tile_b - 1 - tt);
       vm_wait_tiles<LOADS, NB - 2>(ahead);
-      __syncthreads();   // tile tt visible; every wave is done with tile tt - 1 and its P
+      lds_barrier();     // tile tt visible; every wave is done with tile tt - 1 and its P
       if (tt + NB - 1 < tile_b) issue(tt + NB - 1, (tt + NB - 1 - tile_a) % NB);
 
       // ---- S^T = K Q^T for rows [16 w, 16 w + 16), softmax update, P^T to LDS ----
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (any_rescale && q4t == 0) corr_lds[16 * w + l16t] = corr;
         if (lane_t == 0) flag_lds[w] = any_rescale ? 1 : 0;
       }
-      __syncthreads();   // P^T, corrections and flags of tile tt visible
+      lds_barrier();     // P^T, corrections and flags of tile tt visible
 
       // ---- O^T += V^T P^T for channels [VC w, VC w + VC) of all rows ----
       {

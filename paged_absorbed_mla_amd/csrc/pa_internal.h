@@ -30,7 +30,8 @@ struct AttnConfig {
   int hsp, vhsp;   // padded head sizes of the compiled instance
   int nw;          // waves per workgroup
   int kt;          // keys per LDS tile
-  int wide;        // 1: attn_wide_kernel (8 waves, 128-row query tiles); 0: attn_kernel (32 rows per wave)
+  int wide;        // 0: attn_kernel (32 rows per wave); 1: attn_wide_kernel (8 waves, 128-row query tiles);
+                   // 2: attn_mla_kernel (4 waves x 32 rows, query resident in registers)
   int rows() const { return wide ? 128 : 32 * nw; }
 };
 
@@ -43,7 +44,8 @@ struct WsLayout {
   int grid;             // workgroups of the attention launch
   int ranges;           // unit ranges of the schedule (one per workgroup)
   int64_t part_cap;     // partial-result slots
-  size_t off_header, off_wg_range, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  size_t off_header, off_wg_range, off_wg_tile, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  size_t off_qrot;      // rotated query channels [T * H][rd] (0: none)
   size_t total;
 };
 
