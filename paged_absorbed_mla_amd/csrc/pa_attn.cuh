@@ -75,7 +75,9 @@ struct AttnParams {
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
   const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
-  float* part_acc;          // [slots][rows][VHSP]
+  float* part_acc;          // partial accumulators: slot s, row r at s * part_slot + r * part_row
+  int64_t part_slot;        // floats between slots (padded: not a power of two)
+  int part_row;             // floats between rows (VHSP + 4)
   const uint16_t* qrot;     // [T * H][rd]: query rotary channels after RoPE (four-wave 576 kernel)
   int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         ml[0] = st.m_run;
         ml[1] = l_tot;
       }
-      float* acc = p.part_acc + (slot * RW + rloc) * VHSP;
+      float* acc = p.part_acc + slot * p.part_slot + (int64_t)rloc * p.part_row;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -633,48 +635,96 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 // Merge the partials of every query tile that several workgroups processed:
 // with M = max_i m_i (log2 domain) and w_i = 2^(m_i - M),
 // out = sum_i w_i acc_i / sum_i w_i l_i, rounded to nearest even.
-// Grid: (query tiles, rows / kCombineRows); one thread per 4 output channels.
+// Grid: (query tiles, RW / kCombineRows) of 256 threads. TPR threads share a
+// row; thread j of a row owns the 4-channel groups j, j + TPR, j + 2 TPR, ...
+// (so each load instruction covers contiguous bytes of a row). Every thread forms its row's
+// weights itself from the (m, l) pairs (read 8 pieces at a time, so the loads
+// overlap), then accumulates the pieces' slices 4 pieces at a time with all
+// their 16-byte loads in flight together (coalesced across the row's threads).
 constexpr int kCombineRows = 16;
 
 template <typename DT, int VHSP, int RW>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
+  constexpr int TPR = (VHSP / 4) < 16 ? (VHSP / 4) : 16;   // threads per row
+  constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 4)
+  constexpr int ROWS = 256 / TPR;                          // rows per pass
+  constexpr int NV = CPT / 4;
+  constexpr int QM = 8;                                    // pieces per batch of (m, l) loads
+  constexpr int QA = 4;                                    // pieces per batch of accumulator loads
+  static_assert(CPT % 4 == 0 && CPT * TPR == VHSP, "channel split");
   const int i = blockIdx.x;
   if (i >= ld_uniform(p.header + 1)) return;
   const MTile t = ld_uniform_tile(p.mt + i);
   if (t.npieces <= 1) return;
-  constexpr int C4 = VHSP / 4;
-  const int cum_b = ld_uniform(p.cumseq + t.b);
   const int r0 = blockIdx.y * kCombineRows;
-  for (int idx = threadIdx.x; idx < kCombineRows * C4; idx += 256) {
-    const int r = r0 + idx / C4;
-    const int c0 = (idx % C4) * 4;
-    if (r >= t.nrows || c0 >= p.vhs) continue;
-    float mx = -INFINITY;
-    for (int q = 0; q < t.npieces; ++q)
-      mx = fmaxf(mx, p.part_ml[((int64_t)(t.part_base + q) * RW + r) * 2]);
-    float den = 0.0f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < t.npieces; ++q) {
-      const int64_t sr = (int64_t)(t.part_base + q) * RW + r;
-      const float m = p.part_ml[sr * 2];
-      const float wq = (m == -INFINITY) ? 0.0f : fast_exp2(m - mx);
-      den += wq * p.part_ml[sr * 2 + 1];
-      const f32x4_t a = *(const f32x4_t*)(p.part_acc + sr * VHSP + c0);
-      acc += wq * a;
+  if (r0 >= t.nrows) return;
+  const int nq = t.npieces;
+  const int cum_b = ld_uniform(p.cumseq + t.b);
+  for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
+    const int r = r0 + rr;
+    if (r >= t.nrows) continue;
+    const int c0 = (threadIdx.x % TPR) * 4;                 // channel of group 0; group v at c0 + 4 TPR v
+    if (c0 >= p.vhs) continue;
+    const float* ml = p.part_ml + ((int64_t)t.part_base * RW + r) * 2;   // piece q at + q * RW * 2
+    // Reference max and denominator: one batch of (m, l) loads per QM pieces
+    // (the usual case, nq <= QM, is a single round trip).
+    float mx = -INFINITY, den = 0.0f;
+    for (int q0 = 0; q0 < nq; q0 += QM) {
+      float m[QM], l[QM];
+#pragma unroll
+      for (int k = 0; k < QM; ++k) {
+        const bool ok = q0 + k < nq;
+        m[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2] : -INFINITY;
+        l[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2 + 1] : 0.0f;
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < QM; ++k) bm = fmaxf(bm, m[k]);
+      const float nm = fmaxf(mx, bm);
+      den = (mx == -INFINITY) ? 0.0f : den * fast_exp2(mx - nm);
+#pragma unroll
+      for (int k = 0; k < QM; ++k) den += (m[k] == -INFINITY) ? 0.0f : fast_exp2(m[k] - nm) * l[k];
+      mx = nm;
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const int R = t.row0 + r;
-    const int tq = R / p.H;
-    const int h = R - tq * p.H;
-    uint16_t* orow = p.out + ((int64_t)(cum_b + tq) * p.H + h) * p.vhs;
-    if ((p.vhs & 3) == 0) {
-      const uint32_t e0 = DT::from_f32(acc[0] * inv), e1 = DT::from_f32(acc[1] * inv);
-      const uint32_t e2 = DT::from_f32(acc[2] * inv), e3 = DT::from_f32(acc[3] * inv);
-      *(u32x2_t*)(orow + c0) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-    } else {
+    // Weighted sum of the row slices.
+    f32x4_t acc[NV];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (c0 + k < p.vhs) orow[c0 + k] = (uint16_t)DT::from_f32(acc[k] * inv);
+    for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* pa0 = p.part_acc + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;   // piece q at + q * part_slot
+    for (int q0 = 0; q0 < nq; q0 += QA) {
+      f32x4_t a[QA][NV];
+      float wq[QA];
+#pragma unroll
+      for (int k = 0; k < QA; ++k) {
+        const bool ok = q0 + k < nq;
+        const int q = ok ? q0 + k : q0;
+        const f32x4_t* src = (const f32x4_t*)(pa0 + (int64_t)q * p.part_slot);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) a[k][v] = src[v * TPR];
+        const float m = ml[(int64_t)q * RW * 2];
+        wq[k] = (!ok || m == -INFINITY) ? 0.0f : fast_exp2(m - mx) * inv;
+      }
+#pragma unroll
+      for (int k = 0; k < QA; ++k)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += wq[k] * a[k][v];
+    }
+    uint16_t* orow = p.out + ((int64_t)cum_b * p.H + t.row0 + r) * p.vhs + c0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = c0 + 4 * TPR * v;
+      if ((p.vhs & 3) == 0) {
+        if (c < p.vhs) {
+          const uint32_t e0 = DT::from_f32(acc[v][0]), e1 = DT::from_f32(acc[v][1]);
+          const uint32_t e2 = DT::from_f32(acc[v][2]), e3 = DT::from_f32(acc[v][3]);
+          *(u32x2_t*)(orow + 4 * TPR * v) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (c + k < p.vhs) orow[4 * TPR * v + k] = (uint16_t)DT::from_f32(acc[v][k]);
+      }
     }
   }
 }

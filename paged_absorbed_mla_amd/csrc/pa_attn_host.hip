@@ -304,7 +304,11 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_seq_base = off; off = align256(off + (size_t)(g.B + 1) * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
-  L.off_part_acc = off; off = align256(off + (size_t)L.part_cap * RW * cfg.vhsp * sizeof(float));
+  // Partial accumulators: rows padded by 16 bytes and slots by 256 bytes so
+  // concurrent pieces do not sit at power-of-two strides.
+  L.part_row = cfg.vhsp + 4;
+  L.part_slot = (int64_t)RW * L.part_row + 64;
+  L.off_part_acc = off; off = align256(off + (size_t)L.part_cap * L.part_slot * sizeof(float));
   L.off_qrot = 0;
   if (cfg.wide == 2 && g.do_rotary) {
     L.off_qrot = off;
@@ -373,6 +377,8 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.zero16 = (const uint16_t*)sp.zero16;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
   ap.part_acc = (float*)(wsb + ws.off_part_acc);
+  ap.part_slot = ws.part_slot;
+  ap.part_row = ws.part_row;
   ap.qrot = sp.qrot;
   ap.nblk = g.NB;
   ap.prow = g.do_rotary ? g.P : 1;

@@ -622,7 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int k = 0; k < 8 && cg + k < p.vhs; ++k) dst[k] = (uint16_t)DT::from_f32(x[k]);
           }
         } else {
-          float* dst = p.part_acc + (slot * RW + r) * VHSP + cg;
+          float* dst = p.part_acc + slot * p.part_slot + (int64_t)r * p.part_row + cg;
           *(f32x4_t*)dst = v0;
           *(f32x4_t*)(dst + 4) = v1;
         }

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int rb = 0; rb < NRB; ++rb) {
         const int r = 16 * rb + l16e;
         if (r < t.nrows) {
-          float* acc = p.part_acc + (slot * RW + r) * VHSP + VC * w + 4 * q4e;
+          float* acc = p.part_acc + slot * p.part_slot + (int64_t)r * p.part_row + VC * w + 4 * q4e;
 #pragma unroll
           for (int vb = 0; vb < NVB; ++vb) *(f32x4_t*)(acc + 16 * vb) = o[vb][rb];
         }

@@ -46,6 +46,8 @@ struct WsLayout {
   int64_t part_cap;     // partial-result slots
   size_t off_header, off_wg_range, off_wg_tile, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
   size_t off_qrot;      // rotated query channels [T * H][rd] (0: none)
+  int64_t part_slot;    // floats between partial-result slots
+  int part_row;         // floats between partial-result rows
   size_t total;
 };
 
