@@ -51,12 +51,20 @@ namespace pa {
 #ifndef PA_MLA_PAD
 #define PA_MLA_PAD 0
 #endif
+// XOR chunk swizzle of a staged latent row: chunk c of row r sits at
+// position c ^ mla_swizzle(r). Bit 2 comes from row bit 1 and bits 1..0 from
+// row bits 3..2, so both LDS read patterns are free of bank conflicts (64
+// banks of 4 bytes; LDS rows are 1152 bytes, an odd multiple of 128): the
+// 16-lane groups of the K reads (16 consecutive rows, one chunk) and the
+// 32-lane halves of the transposing V reads (4 rows x 4 aligned chunks).
+__device__ __forceinline__ int mla_swizzle(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+
 template <int HSP>
 struct MlaLds {
   static constexpr int CPR = HSP / 8;                   // 16-byte chunks of a latent row
   static constexpr int RCH = CPR + PA_MLA_PAD;          // 16-byte chunks per LDS row
   static constexpr int ROWB = RCH * 16;                 // bytes per LDS row
-  static __device__ __forceinline__ int swz(int row) { return PA_MLA_PAD ? 0 : lds_swizzle(row); }
+  static __device__ __forceinline__ int swz(int row) { return PA_MLA_PAD ? 0 : mla_swizzle(row); }
 };
 
 
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int it = 0; it < LOADS; ++it) {
     const int sl = it * 64 + lane;
     const int k = sl / CPR;
-    const int lc = (sl - k * CPR) ^ lds_swizzle(w * KW + k);
+    const int lc = (sl - k * CPR) ^ mla_swizzle(w * KW + k);
     const uint32_t off = lc * 8 < p.hs ? (uint32_t)((k * p.hs + lc * 8) * 2) : 0xFFFFu;
     const int sh = (it & 1) * 16;
     load_off2[it >> 1] = (load_off2[it >> 1] & ~(0xFFFFu << sh)) | (off << sh);
@@ -481,14 +489,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
       const int ln = opaque_lane();
       const int r32 = ln & 31, h1 = ln >> 5;
-      const int swk = lds_swizzle(r32);
+      const int swk = mla_swizzle(r32);
 #pragma unroll
       for (int r = 0; r < 4; ++r) kaddr[r] = r32 * CPR * 16 + (((2 * r + h1) ^ swk) << 4);
       // V^T (PV A operand), transposing reads: lane (g, jj, cq) supplies row
       // 4 (g >> 1) + jj (and + 8) and channel quad cq of its 16-lane group.
       const int g = ln >> 4, jj = (ln & 15) >> 2, cq = ln & 3;
       const int k0b = (g >> 1) * 4 + jj;
-      const int sw0 = lds_swizzle(k0b), sw1 = lds_swizzle(k0b + 8);
+      const int sw0 = mla_swizzle(k0b), sw1 = mla_swizzle(k0b + 8);
       const int lcb = 2 * (g & 1) + (cq >> 1);
 #pragma unroll
       for (int par = 0; par < 2; ++par) {

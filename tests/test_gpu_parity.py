@@ -204,6 +204,28 @@ def test_edge_case(name):
     _edge(_spec(name=name, **EDGES[name]))
 
 
+# The same method cases at DeepSeek-V3 latent dimensions (576 / 512), which run
+# the wide-row kernel: score-scale sign and zero, softcap, window, float16,
+# decode rows whose keys end inside a tile, and keys that straddle pieces.
+_DSV3 = dict(num_heads=16, head_size=576, v_head_size=512, rotary_dim=64, rotary_offset=512, block_size=16,
+             past=[33, 0, 70], new=[9, 17, 1], scale=0.06)
+DSV3_EDGES = {
+    "dsv3_neg_scale": dict(scale=-0.06),
+    "dsv3_zero_scale": dict(scale=0.0),
+    "dsv3_softcap": dict(softcap=2.0, dtype="f16"),
+    "dsv3_window": dict(local_window_size=20),
+    "dsv3_f16": dict(dtype="f16"),
+    "dsv3_bs64_decode": dict(block_size=64, past=[300, 95, 1], new=[1, 1, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(DSV3_EDGES))
+def test_edge_case_dsv3(name):
+    kw = dict(_DSV3)
+    kw.update(DSV3_EDGES[name])
+    _edge(_spec(name=name, **kw))
+
+
 def test_first_token_and_window0_exact():
     """A token that sees only itself outputs its own value row, bit for bit."""
     torch = _torch()
