@@ -11,9 +11,11 @@ values N(0,1)*0.5, scale 1/sqrt(192). Inputs are seeded synthetic data, resident
 in HBM before timing starts.
 
 Prints one JSON line. `value` is algorithmic TFLOP/s of the step (2 (hs+vhs)
-flops per (token, head, visible key)); `roofline` reports the attention phase
-against the HBM bound (this workload sits below the bf16 MFMA ridge) with the
-phase duration measured live with HIP events on the launch stream;
+flops per (token, head, visible key)); `roofline` reports the dominant kernel
+(the attention kernel) against the HBM bound (this workload sits below the
+bf16 MFMA ridge): the phase's algorithmic bytes over the kernel's duration,
+measured live with HIP events that the library records around that launch on
+its stream, with the whole phase beside it;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -50,6 +52,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the markdown summary of a rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="print the markdown summary of four rocprofv3 --pmc output directories: FETCH_SIZE "
+                         "and WRITE_SIZE of the bench, then of --calibrate-copy")
+    ap.add_argument("--cmd", default="", help="command line recorded in a summary")
     return ap.parse_args()
 
 
@@ -64,6 +72,108 @@ def calibrate_copy(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibration_copy_bytes": n, "reads": n, "writes": n}), flush=True)
+
+
+# The attention kernel the roofline reports on, its source files (any change
+# makes stored HBM counters stale) and the profile that holds its counters.
+DOMINANT_KERNEL = "attn_mla_kernel"
+KERNEL_SOURCES = ["paged_absorbed_mla_amd/csrc/pa_attn_mla.cuh", "paged_absorbed_mla_amd/csrc/pa_attn.cuh",
+                  "paged_absorbed_mla_amd/csrc/pa_device.h", "paged_absorbed_mla_amd/csrc/inst/attnm_bf16_576_512.hip",
+                  "paged_absorbed_mla_amd/build.py"]
+COUNTERS_PROFILE = "profiles/attn_mla_kernel_dsv3_576_512_bf16_decode_b64_hbm_counters.md"
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per dispatch of the dominant kernel from the committed counter
+    summary, or None when it is missing, for another workload, or taken on
+    other kernel sources."""
+    path = os.path.join(ROOT, COUNTERS_PROFILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    i = text.find("```json")
+    if i < 0:
+        return None
+    blob = json.loads(text[i + 7:text.index("```", i + 7)])
+    if blob.get("sources") != kernel_sources_hash() or blob.get("workload") != workload:
+        return None
+    return int(round(blob["fetch_kib"] * 1024 * blob["fetch_scale"] + blob["write_kib"] * 1024 * blob["write_scale"]))
+
+
+def _rocprof_rows(d: str, name: str):
+    import csv
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(name):
+                with open(os.path.join(root, f)) as fh:
+                    return list(csv.DictReader(fh))
+    raise FileNotFoundError(f"no *{name} under {d}")
+
+
+def _short(kname: str) -> str:
+    return kname.split("(")[0].replace("void ", "")
+
+
+def summarize_trace(d: str, cmd: str):
+    rows = _rocprof_rows(d, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| kernel | calls | avg us | min us | max us | share |\n|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    if cmd:
+        print(f"\nCommand: `{cmd}`")
+
+
+def _counter_means(d: str, counter: str):
+    import collections
+    acc = collections.defaultdict(list)
+    for r in _rocprof_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            acc[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_counters(fetch_d: str, write_d: str, cal_fetch_d: str, cal_write_d: str, cmd: str):
+    fetch, nf = _counter_means(fetch_d, "FETCH_SIZE")
+    write, _ = _counter_means(write_d, "WRITE_SIZE")
+    cf, _ = _counter_means(cal_fetch_d, "FETCH_SIZE")
+    cw, _ = _counter_means(cal_write_d, "WRITE_SIZE")
+    copy = [k for k in cf if "copy" in k.lower()]
+    assert copy, f"no copy kernel among {list(cf)}"
+    mib = 1024
+    kib_copied = mib * 1024
+    fs = kib_copied / cf[copy[0]]
+    ws = kib_copied / cw[copy[0]]
+    print(f"Calibration: `{copy[0]}` copies {mib} MiB ({kib_copied:,} KiB read and written); its counters read "
+          f"FETCH_SIZE {cf[copy[0]]:,.0f} KiB and WRITE_SIZE {cw[copy[0]]:,.0f} KiB per dispatch, so the scale "
+          f"factors are {fs:.3f} (fetch) and {ws:.3f} (write).\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB (scaled) | written MB (scaled) |")
+    print("|---|---|---|---|---|---|")
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        wk = write.get(k, float("nan"))
+        print(f"| `{k}` | {nf[k]} | {fetch[k]:,.1f} | {wk:,.1f} | {fetch[k] * 1024 * fs / 1e6:,.1f} | "
+              f"{wk * 1024 * ws / 1e6:,.1f} |")
+    dom = [k for k in fetch if DOMINANT_KERNEL in k]
+    if dom:
+        blob = {"kernel": dom[0], "fetch_kib": round(fetch[dom[0]], 1), "write_kib": round(write[dom[0]], 1),
+                "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "workload": WORKLOADS["c4"],
+                "sources": kernel_sources_hash()}
+        print("\nMachine-readable figures for `bench.py` (`sources` names the kernel sources these counters "
+              "belong to; bench.py reports `traffic` only while they are unchanged):\n")
+        print("```json\n" + json.dumps(blob) + "\n```")
+    if cmd:
+        print(f"\nCommands: {cmd}")
 
 
 def cpu_baseline(w, target_s: float):
@@ -105,6 +215,12 @@ def cpu_baseline(w, target_s: float):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.cmd)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.cmd)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
@@ -114,6 +230,7 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+    import paged_absorbed_mla_amd as pa
     from paged_absorbed_mla_amd import workloads as wl
     from paged_absorbed_mla_amd.device import DeviceWorkload
 
@@ -130,6 +247,12 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Events around the attention kernel itself, recorded by the library on its
+    # launch stream (pa_latent_profile_next); recorded once here so they exist.
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in kev:
+        a_.record(stream)
+        b_.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start_all = torch.cuda.Event(enable_timing=True)
@@ -138,6 +261,7 @@ def main():
     for k in range(args.steps):
         dev.write()
         ev[k][0].record(stream)
+        pa.pa_latent_profile_next(kev[k][0], kev[k][1])
         dev.attention()
         ev[k][1].record(stream)
     end_all.record(stream)
@@ -147,28 +271,38 @@ def main():
     ms_step = ms_total / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in ev]
     attn_avg_ms = float(np.mean(attn_ms))
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_avg_ms = float(np.mean(kern_ms))
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step; "
-          f"attention phase avg {attn_avg_ms:.4f} ms, median {np.median(attn_ms):.4f} ms", file=sys.stderr, flush=True)
+          f"attention phase avg {attn_avg_ms:.4f} ms, median {np.median(attn_ms):.4f} ms; "
+          f"{DOMINANT_KERNEL} avg {kern_avg_ms:.4f} ms", file=sys.stderr, flush=True)
 
     flops = counts["flops"]
     byts = counts["bytes"]
     tflops_step = flops / (ms_step * 1e-3) / 1e12
-    attn_gbs = byts / (attn_avg_ms * 1e-3) / 1e9
-    attn_tflops = flops / (attn_avg_ms * 1e-3) / 1e12
     peak_tf = BF16_PEAK_TFLOPS if w["dtype"] == "bf16" else F16_PEAK_TFLOPS
     hbm_bound = (byts / (HBM_PEAK_GBS * 1e9)) >= (flops / (peak_tf * 1e12))
+    # Roofline of the dominant kernel: the phase's algorithmic bytes (flops) per
+    # launch over the kernel's own average duration.
+    k_gbs = byts / (kern_avg_ms * 1e-3) / 1e9
+    k_tflops = flops / (kern_avg_ms * 1e-3) / 1e12
+    traffic = stored_traffic(WORKLOADS[args.config]) if args.config == "c4" else None
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": round(attn_tflops / peak_tf, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(k_tflops / peak_tf, 4), "traffic": traffic}
+    phase_gbs = byts / (attn_avg_ms * 1e-3) / 1e9
+    phase_tflops = flops / (attn_avg_ms * 1e-3) / 1e12
     roof.update({
-        "kernel": "attention phase: pa_latent_attention (schedule + attn_kernel + combine)",
-        "avg_ms": round(attn_avg_ms, 5),
+        "kernel": f"{DOMINANT_KERNEL} (HIP events on its launch stream)",
+        "avg_ms": round(kern_avg_ms, 5),
         "alg_bytes_per_launch": int(byts), "alg_flops_per_launch": int(flops),
-        "also": {"tflops": round(attn_tflops, 1), "gbs": round(attn_gbs, 1),
-                 "mfma_frac": round(attn_tflops / peak_tf, 4), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "phase": {"what": "pa_latent_attention: schedule + attention + combine", "avg_ms": round(attn_avg_ms, 5),
+                  "gbs": round(phase_gbs, 1), "tflops": round(phase_tflops, 1),
+                  "hbm_frac": round(phase_gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(phase_tflops / peak_tf, 4)},
     })
     out = {
         "metric": "paged-MLA decode attention TFLOP/s + HBM GB/s (% of roofline), 576/512 bf16",

@@ -179,6 +179,16 @@ pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_late
                                      void* output, void* workspace, size_t workspace_bytes,
                                      int32_t split_kv, void* stream);
 
+/* Measurement hook (not part of the method). `before` and `after` are
+ * hipEvent_t handles created by the caller, or NULL. The next
+ * pa_latent_attention / pa_latent_attention_splits call made on this thread
+ * records `before` on its stream immediately before the launch of its
+ * attention kernel and `after` immediately after it, so hipEventElapsedTime
+ * of the pair is that kernel's duration without the schedule and combine
+ * launches around it. The registration is consumed by that call (also when
+ * it fails or launches nothing). Returns PA_OK. */
+pa_status pa_latent_profile_next(void* before, void* after);
+
 /* Message of the last failed call on this thread ("" after a successful call).
  * Valid until the next call into this library on the same thread. */
 const char* pa_last_error(void);

@@ -25,7 +25,7 @@ PA_F16 = 10
 PA_BF16 = 16
 
 EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention",
-            "pa_latent_attention_splits", "pa_last_error", "pa_latent_abi_version")
+            "pa_latent_attention_splits", "pa_latent_profile_next", "pa_last_error", "pa_latent_abi_version")
 
 
 class pa_latent_attrs(ctypes.Structure):
@@ -84,6 +84,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_latent_attention_splits.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                ctypes.c_int32, vp]
     lib.pa_latent_attention_splits.restype = ctypes.c_int
+    lib.pa_latent_profile_next.argtypes = [vp, vp]
+    lib.pa_latent_profile_next.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_latent_abi_version.argtypes = []
@@ -170,6 +172,17 @@ def pa_latent_attention_splits(attrs, dims, dtype, query, key_cache, cos_cache, 
                                         _ptr(block_table), _ptr(output), _ptr(workspace), int(workspace_bytes),
                                         int(split_kv), _stream(stream, output, query))
     return _check(st) if check else st
+
+
+def pa_latent_profile_next(before, after):
+    """Register two events (torch.cuda.Event after one record(), or raw hipEvent_t
+    handles as ints; None for none) to be recorded around the attention kernel of
+    this thread's next pa_latent_attention call."""
+    def handle(ev):
+        if ev is None:
+            return None
+        return ctypes.c_void_p(int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev))
+    return _check(load().pa_latent_profile_next(handle(before), handle(after)))
 
 
 def pa_last_error() -> str:

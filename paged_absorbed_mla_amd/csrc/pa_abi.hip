@@ -117,10 +117,16 @@ pa_status device_error(hipError_t e, const char* what) {
   return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Events registered by pa_latent_profile_next for this thread's next attention call.
+thread_local hipEvent_t g_prof_ev[2] = {nullptr, nullptr};
+
 pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
                          const void* query, const void* key_cache, const void* cos_cache, const void* sin_cache,
                          const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* output,
                          void* workspace, size_t workspace_bytes, bool split_kv, void* stream) {
+  hipEvent_t ev[2] = {g_prof_ev[0], g_prof_ev[1]};
+  g_prof_ev[0] = g_prof_ev[1] = nullptr;
+  const bool timed = ev[0] != nullptr && ev[1] != nullptr;
   pa::CallGeom g;
   pa_status st = resolve(attrs, dims, dtype, &g);
   if (st != PA_OK) return st;
@@ -151,7 +157,7 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   if (workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes, ws.total);
   e = pa::launch_attention(g, cfg, ws, split_kv, query, key_cache, cos_cache, sin_cache, cumseq, past, block_table,
-                           output, workspace, (hipStream_t)stream);
+                           output, workspace, (hipStream_t)stream, timed ? ev : nullptr);
   if (e != hipSuccess) return device_error(e, "attention launch");
   g_last_error.clear();
   return PA_OK;
@@ -223,6 +229,13 @@ pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_late
                                      void* workspace, size_t workspace_bytes, int32_t split_kv, void* stream) {
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, workspace, workspace_bytes, split_kv != 0, stream);
+}
+
+pa_status pa_latent_profile_next(void* before, void* after) {
+  g_prof_ev[0] = (hipEvent_t)before;
+  g_prof_ev[1] = (hipEvent_t)after;
+  g_last_error.clear();
+  return PA_OK;
 }
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }

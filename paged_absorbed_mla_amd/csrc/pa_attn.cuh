@@ -186,6 +186,16 @@ __device__ __forceinline__ float softcap_log2(float s, float scale, float cap, f
   return cap * th * kLog2e;
 }
 
+// Unit range handled by this workgroup. Workgroups are dispatched to the
+// eight XCDs (each with its own L2) round-robin by index, so when the grid is
+// a multiple of eight, XCD x takes the consecutive ranges x * grid/8 ..
+// (x + 1) * grid/8 - 1: ranges that share a query tile, and so read the same
+// query rows, then mostly share an L2.
+__device__ __forceinline__ int range_of_block() {
+  const int g = (int)gridDim.x, b = (int)blockIdx.x;
+  return (g & 7) == 0 ? (b & 7) * (g >> 3) + (b >> 3) : b;
+}
+
 // Scalar (s_load) read of data that no thread writes while the kernel runs:
 // block_table, sequence lengths and the schedule the previous launch wrote.
 __device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
@@ -410,8 +420,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int u = ld_uniform(p.wg_range + blockIdx.x);
-  const int u_end = ld_uniform(p.wg_range + blockIdx.x + 1);
+  const int wr = range_of_block();
+  int u = ld_uniform(p.wg_range + wr);
+  const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;
 
   // Query tile containing unit u: the last i with mt[i].unit0 <= u.
@@ -609,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         }
       }
     } else {
-      const int64_t slot = (int64_t)t.part_base + ((int)blockIdx.x - t.w_first);
+      const int64_t slot = (int64_t)t.part_base + (wr - t.w_first);
       if (hi == 0) {
         float* ml = p.part_ml + (slot * RW + rloc) * 2;
         ml[0] = st.m_run;
@@ -729,27 +740,33 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   }
 }
 
-typedef hipError_t (*AttnLaunchFn)(const AttnParams&, int, bool, int, hipStream_t);
+// Launches the attention kernel (events ev[0] / ev[1] recorded around it when
+// ev is non-null) and, when `combine`, the split-KV combine.
+typedef hipError_t (*AttnLaunchFn)(const AttnParams&, int, bool, int, hipStream_t, const hipEvent_t*);
 typedef hipError_t (*AttnOccFn)(int*);
 
 }  // namespace pa
 
 #define PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, SUF) attn_##DTN##_##HSP##_##VHSP##_##NW##_##KT##_##SUF
-#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT, QREG)                                               \
-  namespace pa {                                                                                            \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                              \
-    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG>;                                            \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0);  \
-  }                                                                                                         \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,         \
-                                                        int cgrid, hipStream_t s) {                           \
-    attn_kernel<DT, HSP, VHSP, NW, KT, QREG><<<grid, NW * 64, 0, s>>>(p);                                         \
-    hipError_t e = hipGetLastError();                                                                       \
-    if (e != hipSuccess || !combine) return e;                                                              \
-    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);                                              \
-    return hipGetLastError();                                                                               \
-  }                                                                                                         \
+#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT, QREG)                                          \
+  namespace pa {                                                                                        \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                          \
+    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG>;                                  \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0); \
+  }                                                                                                     \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,     \
+                                                        int cgrid, hipStream_t s, const hipEvent_t* ev) { \
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                          \
+    if (e != hipSuccess) return e;                                                                      \
+    attn_kernel<DT, HSP, VHSP, NW, KT, QREG><<<grid, NW * 64, 0, s>>>(p);                               \
+    e = hipGetLastError();                                                                              \
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                            \
+    if (e != hipSuccess || !combine) return e;                                                          \
+    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);         \
+    return hipGetLastError();                                                                           \
+  }                                                                                                     \
   }
 #define PA_DECLARE_ATTN_INSTANCE(DTN, HSP, VHSP, NW, KT)                                                    \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams&, int, bool, int, hipStream_t);    \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams&, int, bool, int, hipStream_t,     \
+                                                       const hipEvent_t*);                                  \
   hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int*);

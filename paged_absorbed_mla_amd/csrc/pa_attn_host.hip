@@ -20,6 +20,7 @@ struct SchedParams {
   const int32_t* cumseq;
   const int32_t* past;
   int B, H, RW, KT, window, grid, split_kv;
+  int piece_units;   // virtual KV tiles charged at the start of every query tile
   // Query RoPE pre-pass (blocks 1..): qrot[t * H + h][0 : rd] = RoPE of the
   // query channels [ro, ro + rd) of (t, h), rounded to the storage type.
   const uint16_t* query;
@@ -32,7 +33,7 @@ struct SchedParams {
   int32_t* header;
   int32_t* wg_range;
   int32_t* wg_tile;
-  int32_t* seq_base;
+  int32_t* sched;    // global scratch for the arrays below when they exceed kSchedLdsInts
   MTile* mt;
   uint32_t* zero16;
 };
@@ -88,119 +89,173 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
 
 // Blocks 1.. of the schedule launch: RoPE of the query's rotary channels into
 // the workspace, one 8-channel chunk per thread (float32 math, nearest-even
-// rounding; same rotation as the write phase applies to key rows).
+// rounding; same rotation as the write phase applies to key rows). `cum` and
+// `pst` are cumulative_sequence_length and past_seqlens (staged in LDS when
+// they fit).
 template <typename DT>
-__device__ void query_rope_chunk(const SchedParams& p, int64_t idx) {
+__device__ void query_rope_chunk(const SchedParams& p, int64_t idx, const int32_t* cum, const int32_t* pst) {
   const int cpr = p.rd >> 3;                      // rotary chunks per row
   const int64_t row = idx / cpr;                  // t * H + h
   const int c0 = p.ro + (int)(idx - row * cpr) * 8;
   const int64_t t = row / p.H;
-  const int b = find_seq(p.cumseq, p.B, t);
-  const int64_t pos = min(max((int64_t)p.past[b] + (t - (int64_t)p.cumseq[b]), (int64_t)0), p.prow - 1);
   const uint16_t* qrow = p.query + row * p.hs;
   float x[8];
   unpack8<DT>(*(const u32x4_t*)(qrow + c0), x);
+  const int b = find_seq(cum, p.B, t);
+  const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
   rope_chunk<DT>(x, qrow, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
   *(u32x4_t*)(p.qrot + row * p.rd + (c0 - p.ro)) = pack8<DT>(x);
 }
 
+// Block 0 keeps its working arrays (sequence bounds, per-tile unit counts and
+// prefix sums, workgroup ranges) in LDS, so each dependent step (scans and
+// binary searches) costs LDS latency instead of a global round trip; larger
+// problems fall back to the same arrays in the workspace.
+constexpr int kSchedLdsInts = 12288;
+
+__device__ __forceinline__ int64_t sched_ints(int B, int64_t max_mtiles, int grid) {
+  return 3 * (int64_t)B + 2 + 2 * max_mtiles + 1 + grid + 1;
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
+  __shared__ int32_t lds_arr[kSchedLdsInts];
   if (blockIdx.x > 0) {
+    // Token -> sequence search over LDS copies of the sequence bounds (one
+    // coalesced load per block instead of a chain of dependent global loads).
+    const bool staged = 2 * p.B + 1 <= kSchedLdsInts;
+    if (staged) {
+      for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
+        lds_arr[b] = p.cumseq[b];
+        if (b < p.B) lds_arr[p.B + 1 + b] = p.past[b];
+      }
+      __syncthreads();
+    }
+    const int32_t* cum = staged ? lds_arr : p.cumseq;
+    const int32_t* pst = staged ? lds_arr + p.B + 1 : p.past;
     const int64_t n = p.T * p.H * (p.rd >> 3);
     const int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x;
     if (idx < n) {
-      if (p.dtype == 16) query_rope_chunk<BF16>(p, idx);
-      else query_rope_chunk<F16>(p, idx);
+      if (p.dtype == 16) query_rope_chunk<BF16>(p, idx, cum, pst);
+      else query_rope_chunk<F16>(p, idx, cum, pst);
     }
     return;
   }
+  const bool in_lds = sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts;
+  int32_t* const base = in_lds ? lds_arr : p.sched;
+  int32_t* const cum = base;                           // [B + 1] cumulative_sequence_length
+  int32_t* const pst = cum + (p.B + 1);                // [B] past lengths (negative -> 0)
+  int32_t* const sbase = pst + p.B;                    // [B + 1] first query tile of each sequence
+  int32_t* const u0 = sbase + (p.B + 1);               // [max_mtiles + 1] KV tiles, then first unit
+  int32_t* const np = u0 + (p.max_mtiles + 1);        // [max_mtiles] workgroups per query tile
+  int32_t* const wr = np + p.max_mtiles;               // [grid + 1] unit range of every workgroup
+
   if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
-  // A. query tiles per sequence, prefix-summed into seq_base.
+  for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
+    cum[b] = p.cumseq[b];
+    if (b < p.B) pst[b] = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
+  }
+  __syncthreads();
+  // A. query tiles per sequence, prefix-summed into sbase.
   const int64_t M_all = block_exclusive_scan(
       p.B,
       [&](int64_t b) -> int64_t {
-        const int64_t rows = (int64_t)(p.cumseq[b + 1] - p.cumseq[b]) * p.H;
+        const int64_t rows = (int64_t)(cum[b + 1] - cum[b]) * p.H;
         return (rows + p.RW - 1) / p.RW;
       },
-      [&](int64_t b, int64_t v) { p.seq_base[b] = (int32_t)v; });
+      [&](int64_t b, int64_t v) { sbase[b] = (int32_t)v; });
   // M cannot exceed max_mtiles when cumseq[B] = T (a precondition); clamp so a
   // violated precondition cannot write past the tile table.
   const int64_t M = min(M_all, p.max_mtiles);
-  if (threadIdx.x == 0) p.seq_base[p.B] = (int32_t)M_all;
+  if (threadIdx.x == 0) sbase[p.B] = (int32_t)M_all;
   __syncthreads();
-  // B. describe every query tile; its KV tile count goes to unit0 for now.
+  // B. describe every query tile; its KV tile count goes to u0 for now.
   for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
-    int lo = 0, hi = p.B - 1;  // last b with seq_base[b] <= i
+    int lo = 0, hi = p.B - 1;  // last b with sbase[b] <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (p.seq_base[mid] <= i) lo = mid; else hi = mid - 1;
+      if (sbase[mid] <= i) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int rows = (p.cumseq[b + 1] - p.cumseq[b]) * p.H;
-    const int row0 = (int)(i - p.seq_base[b]) * p.RW;
+    const int rows = (cum[b + 1] - cum[b]) * p.H;
+    const int row0 = (int)(i - sbase[b]) * p.RW;
     const int nrows = min(p.RW, rows - row0);
-    const int past_b = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
-    const int pos0 = past_b + row0 / p.H;
-    const int pos1 = past_b + (row0 + nrows - 1) / p.H;
+    const int pos0 = pst[b] + row0 / p.H;
+    const int pos1 = pst[b] + (row0 + nrows - 1) / p.H;
     const int kv_hi = pos1 + 1;
     const int kv_lo = p.window >= 0 ? max(0, pos0 - p.window) : 0;
-    MTile t;
-    t.b = b;
-    t.row0 = row0;
-    t.nrows = nrows;
-    t.kv_lo = kv_lo;
-    t.kv_hi = kv_hi;
-    t.unit0 = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
-    t.part_base = -1;
-    t.w_first = 0;
-    t.npieces = 1;
-    t.pad[0] = t.pad[1] = t.pad[2] = 0;
-    p.mt[i] = t;
+    MTile* t = p.mt + i;
+    t->b = b;
+    t->row0 = row0;
+    t->nrows = nrows;
+    t->kv_lo = kv_lo;
+    t->kv_hi = kv_hi;
+    u0[i] = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
   }
   __syncthreads();
   // C. units: prefix sum of KV tiles.
   const int64_t U = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { return p.mt[i].unit0; },
-      [&](int64_t i, int64_t v) { p.mt[i].unit0 = (int32_t)v; });
+      M, [&](int64_t i) -> int64_t { return u0[i]; }, [&](int64_t i, int64_t v) { u0[i] = (int32_t)v; });
+  if (threadIdx.x == 0) u0[M] = (int32_t)U;
+  __syncthreads();
+  // D. unit range of every workgroup. Split-KV: the units are laid out with
+  // piece_units virtual units before each query tile (the cost of the query
+  // load and epilogue a piece adds), and the virtual line is cut evenly; a
+  // workgroup that enters a second query tile thus takes fewer KV tiles. A
+  // cut inside a tile's virtual prefix falls on the tile's first unit.
+  // Empty ranges sit only at the end or right before a tile's first
+  // workgroup, so the workgroups that share a query tile are consecutive and
+  // each of them writes its partial slot.
+  const int64_t alpha = p.piece_units;
+  const int64_t Uv = U + alpha * M;
+  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
+    int32_t v;
+    if (!p.split_kv) {
+      v = u0[min((int64_t)w, M)];
+    } else if (M == 0) {
+      v = 0;
+    } else {
+      const int64_t x = Uv >= p.grid ? ((int64_t)w * Uv) / p.grid : min((int64_t)w, Uv);
+      int64_t lo = 0, hi = M - 1;   // last tile whose virtual start is <= x
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (u0[mid] + alpha * mid <= x) lo = mid; else hi = mid - 1;
+      }
+      const int64_t o = x - (u0[lo] + alpha * lo);
+      v = (int32_t)min(u0[lo] + max(o - alpha, (int64_t)0), (int64_t)u0[lo + 1]);
+    }
+    wr[w] = v;
+    p.wg_range[w] = v;
+  }
+  __syncthreads();
+  // E. pieces per query tile, and the query tile holding each workgroup's
+  // first unit (the last i with u0[i] <= wr[w]).
+  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
+    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
+    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
+    np[i] = w1 - w0 + 1;
+    p.mt[i].unit0 = u0[i];
+    p.mt[i].w_first = w0;
+    p.mt[i].npieces = w1 - w0 + 1;
+  }
+  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
+    const int uw = wr[w];
+    int64_t lo = 0, hi = M > 0 ? M - 1 : 0;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (u0[mid] <= uw) lo = mid; else hi = mid - 1;
+    }
+    p.wg_tile[w] = (int32_t)lo;
+  }
   if (threadIdx.x == 0) {
     MTile s = {};
     s.unit0 = (int32_t)U;
     p.mt[M] = s;
   }
   __syncthreads();
-  // D. unit range of every workgroup.
-  // Empty ranges only ever sit at the end, so the workgroups that share a query
-  // tile are consecutive and each of them writes its partial slot.
-  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
-    int32_t v;
-    if (!p.split_kv) v = p.mt[min((int64_t)w, M)].unit0;
-    else if (U >= p.grid) v = (int32_t)(((int64_t)w * U) / p.grid);
-    else v = (int32_t)min((int64_t)w, U);
-    p.wg_range[w] = v;
-  }
-  __syncthreads();
-  // E. pieces per query tile, and the query tile holding each workgroup's
-  // first unit (the last i with mt[i].unit0 <= wg_range[w]).
-  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
-    const int w0 = wg_of_unit(p.wg_range, p.grid, p.mt[i].unit0);
-    const int w1 = wg_of_unit(p.wg_range, p.grid, p.mt[i + 1].unit0 - 1);
-    p.mt[i].w_first = w0;
-    p.mt[i].npieces = w1 - w0 + 1;
-  }
-  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
-    const int uw = p.wg_range[w];
-    int64_t lo = 0, hi = M > 0 ? M - 1 : 0;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (p.mt[mid].unit0 <= uw) lo = mid; else hi = mid - 1;
-    }
-    p.wg_tile[w] = (int32_t)lo;
-  }
-  __syncthreads();
   // F. partial slots for the tiles that several workgroups share.
   const int64_t slots = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { const int n = p.mt[i].npieces; return n > 1 ? n : 0; },
-      [&](int64_t i, int64_t v) { p.mt[i].part_base = p.mt[i].npieces > 1 ? (int32_t)v : -1; });
+      M, [&](int64_t i) -> int64_t { const int n = np[i]; return n > 1 ? n : 0; },
+      [&](int64_t i, int64_t v) { p.mt[i].part_base = np[i] > 1 ? (int32_t)v : -1; });
   if (threadIdx.x == 0) {
     p.header[0] = (int32_t)U;
     p.header[1] = (int32_t)M;
@@ -213,8 +268,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 // Instance table
 // ---------------------------------------------------------------------------
 
-PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 8, 32)
-PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 8, 32)
 PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 4, 32)
 PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 4, 32)
 PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
@@ -237,7 +290,6 @@ struct InstanceEntry {
    &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)}
 
 static const InstanceEntry kInstances[] = {
-    PA_ENTRY(16, bf16, 576, 512, 8, 32),  PA_ENTRY(10, f16, 576, 512, 8, 32),
     PA_ENTRY(16, bf16, 576, 512, 4, 32),  PA_ENTRY(10, f16, 576, 512, 4, 32),
     PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
     PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
@@ -254,9 +306,10 @@ static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
   cfg->wide = 0;
+  cfg->piece_units = 2;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 8; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
@@ -301,7 +354,8 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_zero = off; off = align256(off + 16);
   L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
   L.off_wg_tile = off; off = align256(off + (size_t)L.ranges * sizeof(int32_t));
-  L.off_seq_base = off; off = align256(off + (size_t)(g.B + 1) * sizeof(int32_t));
+  L.sched_ints = 3 * g.B + 2 + 2 * L.max_mtiles + 1 + L.ranges + 1;
+  L.off_sched = off; off = align256(off + (size_t)L.sched_ints * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
   // Partial accumulators: rows padded by 16 bytes and slots by 256 bytes so
@@ -321,7 +375,7 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
 hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
                             const void* query, const void* cache, const void* cos_t, const void* sin_t,
                             const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* out,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, const hipEvent_t* ev) {
   if (g.T == 0) return hipSuccess;
   const InstanceEntry* e = find_instance(g.dtype, cfg);
   if (!e) return hipErrorInvalidValue;
@@ -341,7 +395,8 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.header = (int32_t*)(wsb + ws.off_header);
   sp.wg_range = (int32_t*)(wsb + ws.off_wg_range);
   sp.wg_tile = (int32_t*)(wsb + ws.off_wg_tile);
-  sp.seq_base = (int32_t*)(wsb + ws.off_seq_base);
+  sp.sched = (int32_t*)(wsb + ws.off_sched);
+  sp.piece_units = split_kv ? cfg.piece_units : 0;
   sp.mt = (MTile*)(wsb + ws.off_mtiles);
   sp.zero16 = (uint32_t*)(wsb + ws.off_zero);
   sp.query = (const uint16_t*)query;
@@ -396,7 +451,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.scale_log2 = g.scale * kLog2e;
   ap.softcap = g.softcap > 0.0f ? g.softcap : 0.0f;
   ap.softcap_inv = g.softcap > 0.0f ? 1.0f / g.softcap : 0.0f;
-  return e->launch(ap, ws.grid, split_kv, (int)ws.max_mtiles, stream);
+  return e->launch(ap, ws.grid, split_kv, (int)ws.max_mtiles, stream, ev);
 }
 
 }  // namespace pa

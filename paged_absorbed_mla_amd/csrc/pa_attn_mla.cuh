@@ -351,10 +351,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int u = ld_uniform(p.wg_range + blockIdx.x);
-  const int u_end = ld_uniform(p.wg_range + blockIdx.x + 1);
+  const int wr = range_of_block();
+  int u = ld_uniform(p.wg_range + wr);
+  const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;
-  int i = ld_uniform(p.wg_tile + blockIdx.x);   // query tile holding unit u
+  int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
   const bool softcap_on = p.softcap > 0.0f;
 
   // Copy slot sl = it * 64 + lane of this wave is LDS row 8 w + sl / CPR,
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float* const ost = (float*)lds_raw;
     float* const rowl = ost + RW * ORS;                    // [RW] denominators
     if (hi == 0) rowl[rloc] = l_tot;
-    const int64_t slot = whole ? 0 : (int64_t)t.part_base + ((int)blockIdx.x - t.w_first);
+    const int64_t slot = whole ? 0 : (int64_t)t.part_base + (wr - t.w_first);
     if (!whole && hi == 0 && row_ok) {
       float* ml = p.part_ml + (slot * RW + rloc) * 2;
       ml[0] = st.m_ref;
@@ -645,18 +646,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 }  // namespace pa
 
-#define PA_DEFINE_ATTN_MLA_INSTANCE(DT, DTN, HSP, VHSP)                                                      \
-  namespace pa {                                                                                            \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, occ)(int* n) {                                               \
-    void (*fn)(AttnParams) = attn_mla_kernel<DT, HSP, VHSP>;                                                \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), 256, 0);      \
-  }                                                                                                         \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, launch)(const AttnParams& p, int grid, bool combine,          \
-                                                       int cgrid, hipStream_t s) {                          \
-    attn_mla_kernel<DT, HSP, VHSP><<<grid, 256, 0, s>>>(p);                                                 \
-    hipError_t e = hipGetLastError();                                                                       \
-    if (e != hipSuccess || !combine) return e;                                                              \
-    combine_kernel<DT, VHSP, 128><<<dim3(cgrid, 128 / kCombineRows), 256, 0, s>>>(p);                       \
-    return hipGetLastError();                                                                               \
-  }                                                                                                         \
+#define PA_DEFINE_ATTN_MLA_INSTANCE(DT, DTN, HSP, VHSP)                                                 \
+  namespace pa {                                                                                        \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, occ)(int* n) {                                           \
+    void (*fn)(AttnParams) = attn_mla_kernel<DT, HSP, VHSP>;                                            \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), 256, 0);  \
+  }                                                                                                     \
+  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, launch)(const AttnParams& p, int grid, bool combine,      \
+                                                       int cgrid, hipStream_t s, const hipEvent_t* ev) { \
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                          \
+    if (e != hipSuccess) return e;                                                                      \
+    attn_mla_kernel<DT, HSP, VHSP><<<grid, 256, 0, s>>>(p);                                             \
+    e = hipGetLastError();                                                                              \
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                            \
+    if (e != hipSuccess || !combine) return e;                                                          \
+    combine_kernel<DT, VHSP, 128><<<dim3(cgrid, 128 / kCombineRows), 256, 0, s>>>(p);                   \
+    return hipGetLastError();                                                                           \
+  }                                                                                                     \
   }

@@ -30,8 +30,9 @@ struct AttnConfig {
   int hsp, vhsp;   // padded head sizes of the compiled instance
   int nw;          // waves per workgroup
   int kt;          // keys per LDS tile
-  int wide;        // 0: attn_kernel (32 rows per wave); 1: attn_wide_kernel (8 waves, 128-row query tiles);
+  int wide;        // 0: attn_kernel (32 rows per wave);
                    // 2: attn_mla_kernel (4 waves x 32 rows, query resident in registers)
+  int piece_units; // scheduling cost of one extra piece (query load and epilogue), in KV tiles
   int rows() const { return wide ? 128 : 32 * nw; }
 };
 
@@ -44,7 +45,8 @@ struct WsLayout {
   int grid;             // workgroups of the attention launch
   int ranges;           // unit ranges of the schedule (one per workgroup)
   int64_t part_cap;     // partial-result slots
-  size_t off_header, off_wg_range, off_wg_tile, off_seq_base, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  int64_t sched_ints;   // scheduler scratch (int32) when it does not fit its LDS
   size_t off_qrot;      // rotated query channels [T * H][rd] (0: none)
   int64_t part_slot;    // floats between partial-result slots
   int part_row;         // floats between partial-result rows
@@ -56,10 +58,11 @@ hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, 
 
 WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv);
 
-// Attention phase: schedule, attention, combine (three launches).
+// Attention phase: schedule, attention, combine (three launches). `ev`: null, or
+// two events recorded right before and after the attention kernel's launch.
 hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
                             const void* query, const void* cache, const void* cos_t, const void* sin_t,
                             const int32_t* cumseq, const int32_t* past, const int32_t* block_table,
-                            void* out, void* workspace, hipStream_t stream);
+                            void* out, void* workspace, hipStream_t stream, const hipEvent_t* ev);
 
 }  // namespace pa
