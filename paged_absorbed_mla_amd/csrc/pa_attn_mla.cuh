@@ -103,6 +103,14 @@ __device__ __forceinline__ void ds_write_b128_acc(uint32_t addr, f32x4_t v) {
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "a"(v), "n"(OFF) : "memory");
 }
 
+// ds_write_b128 of four VGPRs at LDS address addr + OFF (completion is
+// awaited with lgkmcnt(0), e.g. by lds_barrier()).
+template <int OFF>
+__device__ __forceinline__ void ds_write_b128_v(uint32_t addr, u32x4_t v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
+}
+
 // One 16-byte-per-lane direct global->LDS copy: lane l's 16 bytes at buffer
 // offset voff land at LDS address lds_base + 16 l. Issued as inline assembly
 // so that the compiler does not see an LDS write it cannot order: it would
@@ -159,7 +167,7 @@ struct MlaState {
   static constexpr int NKS = HSP / 16;
   static constexpr int NMT = VHSP / 32;
   u32x4_t qf[NKS];      // query rows as MFMA B fragments (k-step s: channels 16 s + 8 hi .. + 8)
-  f32x16_t o[NMT];      // O^T accumulators, 32-channel blocks
+  f32x16_t o[NMT];      // O^T accumulators: o[4 c + r] = this wave's channel block c x row block r
   float m_ref;          // row's fixed reference (log2 units): -inf until its first visible key
   float m_seen;         // row's running maximum score (log2 units)
   float l_run;          // partial denominator sum of 2^(s - m_ref) over this lane's keys
@@ -181,11 +189,14 @@ template <> struct PRange<F16> { static constexpr float value = 15.0f; };
 
 // S^T = K Q^T for one 32-key tile at LDS address L. A = 32 keys x 16 channels
 // (row l32, chunk 2 s + hi; chunks 8 apart share the swizzle, so the address
-// is kaddr[s & 3] + 128 (s >> 2)). The reads run QPF k-steps ahead and each
-// MFMA waits only for its own read. The LOADS copy instructions of a later
-// tile (`copy`) are spread over the steps, one every NKS / LOADS MFMAs.
-template <typename DT, int HSP, int LOADS, typename Copy>
-__device__ __forceinline__ f32x16_t mla_qk(const u32x4_t* qf, uint32_t L, const uint32_t (&kaddr)[4], Copy&& copy) {
+// is kaddr[s & 3] + 128 (s >> 2)). The reads run QPF k-steps ahead; one wait
+// (in place on the two read destinations) covers the reads of k-steps s and
+// s + 1, so there is one wait per two MFMAs. The LOADS copy instructions of a
+// later tile (`copy`) are spread over the steps, one every NKS / LOADS MFMAs,
+// and between(s) runs after MFMA s (the previous tile's softmax steps).
+template <typename DT, int HSP, int LOADS, typename Copy, typename Between>
+__device__ __forceinline__ f32x16_t mla_qk(const u32x4_t* qf, uint32_t L, const uint32_t (&kaddr)[4], Copy&& copy,
+                                           Between&& between) {
   constexpr int NKS = HSP / 16;
   constexpr int QPF = PA_MLA_QPF;
   constexpr int CSTRIDE = NKS / LOADS;
@@ -196,132 +207,199 @@ __device__ __forceinline__ f32x16_t mla_qk(const u32x4_t* qf, uint32_t L, const 
     constexpr int s = decltype(S)::value;
     ka[s] = ds_read_b128_asm<(s >> 2) * 128>(L + kaddr[s & 3]);
   });
+  static_assert(QPF % 2 == 0 && NKS % 2 == 0, "k-steps waited for in pairs");
   static_for<0, NKS>([&](auto S) {
     constexpr int s = decltype(S)::value;
-    constexpr int newer = (NKS - 1 - s) < (QPF - 1) ? (NKS - 1 - s) : (QPF - 1);
-    const u32x4_t cur = lgkm_wait_v<newer>(ka[s % QPF]);
-    sacc = DT::mfma32(cur, qf[s], sacc);
+    if constexpr (s % 2 == 0) {
+      // Reads issued so far: k-steps 0 .. min(s + QPF - 1, NKS - 1).
+      constexpr int last = (s + QPF - 1) < (NKS - 1) ? (s + QPF - 1) : (NKS - 1);
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(ka[s % QPF]), "+v"(ka[(s + 1) % QPF]) : "n"(last - (s + 1)));
+    }
+    sacc = DT::mfma32(ka[s % QPF], qf[s], sacc);
     if constexpr (s + QPF < NKS) ka[s % QPF] = ds_read_b128_asm<((s + QPF) >> 2) * 128>(L + kaddr[(s + QPF) & 3]);
     if constexpr (s % CSTRIDE == CSTRIDE - 1 && s / CSTRIDE < LOADS) copy(std::integral_constant<int, s / CSTRIDE>{});
+    between(S);
   });
   return sacc;
 }
 
-// O^T += V^T P^T for the tile at LDS address Lv with probabilities pf_in
-// (DO_PV), and the softmax of the scores `sacc` of the tile at key0 into
-// pf_out (DO_SM), its steps placed between the PV MFMAs.
-//   PV: A = 32 channels x 16 keys via two transposing reads (step n: k-step
-//   n / NMT, channel block n % NMT); k-index 8 g + e of lane group g is key
-//   4 g + (e & 3) + 8 (e >> 2), the key order of the S^T accumulator, so P^T
-//   comes straight from the softmax registers.
-//   Softmax: lane holds row l32 and keys hi*4 + (e & 3) + 8 (e >> 2) of the
-//   tile. Fixed reference: the row's first tile with a visible key sets m_ref
-//   (the accumulators are still zero then, so nothing needs rescaling); later
-//   probabilities are 2^(s - m_ref), which may exceed 1, numerator and
-//   denominator share the reference, so the quotient is unchanged. A score
-//   more than PRange above the reference flags the piece for a second pass
-//   with the row's exact maximum as reference (the accumulators are never
-//   rescaled in place).
-template <typename DT, int HSP, int VHSP, bool DO_PV, bool DO_SM>
-__device__ __forceinline__ void mla_pv_softmax(MlaState<HSP, VHSP>& st, uint32_t Lv, const uint32_t (&vaddr)[4],
-                                               const u32x4_t (&pf_in)[2], f32x16_t sacc, int key0, int pos,
-                                               int lo_row, bool softcap_on, const AttnParams& p, u32x4_t (&pf_out)[2]) {
-  constexpr int CPR = HSP / 8;
-  constexpr int NMT = VHSP / 32;
-  constexpr int VPF = PA_MLA_VPF;
-  constexpr int VSTEPS = 2 * NMT;
-  const int lane = threadIdx.x & 63;
-  const int hi = lane >> 5;
-
-  auto v_frag = [&](auto NN) -> u32x4_t {
-    constexpr int n = decltype(NN)::value;
-    constexpr int k2 = n / NMT, mt = n % NMT;
-    constexpr int off = k2 * 16 * MlaLds<HSP>::ROWB + (mt >> 1) * 128;
-    const u32x2_t r0 = ds_read_tr16_b64_asm<off>(Lv + vaddr[mt & 1]);
-    const u32x2_t r1 = ds_read_tr16_b64_asm<off>(Lv + vaddr[2 + (mt & 1)]);
-    return u32x4_t{r0[0], r0[1], r1[0], r1[1]};
-  };
-  u32x4_t va[VPF];
-  if constexpr (DO_PV) {
-    static_for<0, VPF>([&](auto N) { va[decltype(N)::value] = v_frag(N); });
-    // VALU writes of P (SrcB) precede the first PV MFMA.
-    asm volatile("s_nop 4");
+// Static order of the LDS reads of one PV step (32 MFMAs; MFMA n covers
+// k-step ks = n / 16, the wave's channel block c = (n / 4) % 4 and row block
+// r = n % 4). P fragments: the four of a k-step are read together, those of
+// k-step 1 during steps 8..11. V^T fragments (two reads each): two channel
+// blocks ahead. Issued before MFMA 0: P(0, 0..3), V(0, 0), V(0, 1) (8 reads).
+// wait(n) is the number of LDS reads that may still be in flight when MFMA n
+// issues (reads complete in order), capped at the 4-bit lgkmcnt field.
+struct PvSched {
+  static constexpr int kPre = 8;
+  static constexpr int at(int m) {   // reads issued right after MFMA m
+    return m == 8 ? 4 : ((m == 0 || m == 4 || m == 10 || m == 12 || m == 16 || m == 20) ? 2 : 0);
   }
+  static constexpr int before(int n) {
+    int t = kPre;
+    for (int m = 0; m < n; ++m) t += at(m);
+    return t;
+  }
+  static constexpr int endV(int ks, int c) {   // reads issued up to and including V(ks, c)
+    return ks == 0 ? (c == 0 ? 6 : c == 1 ? 8 : c == 2 ? before(1) : before(5))
+                   : (c == 0 ? before(8) + 2 : before(8 + 4 * c + 1));
+  }
+  static constexpr int endP(int ks, int r) {
+    return ks == 0 ? r + 1 : (r < 2 ? before(8) + 3 + r : before(10) + r - 1);
+  }
+  static constexpr int wait(int n) {
+    const int ks = n / 16, c = (n / 4) % 4, r = n % 4;
+    const int e = endV(ks, c) > endP(ks, r) ? endV(ks, c) : endP(ks, r);
+    const int w = before(n) - e;
+    return w > 15 ? 15 : w;
+  }
+};
+static_assert(PvSched::wait(0) >= 0 && PvSched::wait(16) >= 0 && PvSched::wait(31) >= 0, "read order");
 
-  // Softmax state shared by the chunks below.
-  float tmax = -INFINITY, m_use = 0.0f, psum = 0.0f;
-  float pv[16];
-  const bool full_tile = key0 >= lo_row && key0 + 31 <= pos;
-  // Chunk c of the softmax; chunks are ordered by data dependence.
-  auto sm_chunk = [&](auto C) {
-    constexpr int c = decltype(C)::value;
-    if constexpr (c == 0) {
-      // scale (and softcap) into log2 units
-      if (softcap_on) {
+// Softmax of one tile for this wave's 32 rows, in kSmChunks steps that the
+// caller spreads over the MFMAs of a PV step. Lane holds row l32 and keys hi*4 + (e & 3) + 8 (e >> 2) of the tile.
+// Fixed reference: the row's first tile with a visible key sets m_ref (the
+// accumulators are still zero then, so nothing needs rescaling); later
+// probabilities are 2^(s - m_ref), which may exceed 1, numerator and
+// denominator share the reference, so the quotient is unchanged. A score more
+// than PRange above the reference flags the piece for a second pass with the
+// row's exact maximum as reference (the accumulators are never rescaled in
+// place). full_tile (uniform): every key of the tile is visible to every
+// valid row of the wave, so no per-lane mask is formed.
+struct MlaSm {
+  f32x16_t s;        // scores of the tile, log2 units after step 0
+  float tmax, m_use, psum;
+  u32x4_t pf[2];     // probabilities as PV B fragments (k-steps 0 and 1), packed as they are formed
+};
+constexpr int kSmChunks = 12;
+
+template <typename DT, int HSP, int VHSP, int C>
+__device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm, int key0, int pos, int lo_row,
+                                             bool full_tile, bool softcap_on, const AttnParams& p) {
+  const int hi = (threadIdx.x & 63) >> 5;
+  if constexpr (C == 0) {
+    // scale (and softcap) into log2 units
+    sm.tmax = -INFINITY;
+    sm.psum = 0.0f;
+    if (softcap_on) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = softcap_log2(sacc[e], p.scale, p.softcap, p.softcap_inv);
-      } else {
-        sacc *= p.scale_log2;
-      }
-    } else if constexpr (c == 1) {
-      // mask and tile max
-      if (full_tile) {
+      for (int e = 0; e < 16; ++e) sm.s[e] = softcap_log2(sm.s[e], p.scale, p.softcap, p.softcap_inv);
+    } else {
+      const float c = p.scale_log2;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = key0 + hi * 4 + (e & 3) + 8 * (e >> 2);
-          const float v = (j <= pos && j >= lo_row) ? sacc[e] : -INFINITY;
-          sacc[e] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      }
-    } else if constexpr (c == 2) {
-      tmax = max_xor32(tmax);
-      st.m_seen = fmaxf(st.m_seen, tmax);
-      if (st.m_ref == -INFINITY) st.m_ref = tmax;
-      st.ovf |= tmax > st.m_ref + PRange<DT>::value;
-      m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-    } else if constexpr (c >= 3 && c < 11) {
-      constexpr int k = c - 3;   // probabilities of elements 2k, 2k + 1
-      pv[2 * k] = fast_exp2(sacc[2 * k] - m_use);
-      pv[2 * k + 1] = fast_exp2(sacc[2 * k + 1] - m_use);
-      psum += pv[2 * k] + pv[2 * k + 1];
-    } else if constexpr (c == 11) {
-      float lo[8], hi8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] = pv[e];
-        hi8[e] = pv[8 + e];
-      }
-      pf_out[0] = pack8<DT>(lo);
-      pf_out[1] = pack8<DT>(hi8);
-      st.l_run += psum;
+      for (int e = 0; e < 16; ++e) sm.s[e] *= c;
     }
-  };
-  constexpr int NCHUNK = 12;
-
-  if constexpr (DO_PV) {
-    // Softmax chunk c runs after PV step 2 c + 1 (all chunks fit in the steps).
-    static_assert(2 * NCHUNK <= VSTEPS, "softmax chunks fit between the PV steps");
-    static_for<0, VSTEPS>([&](auto N) {
-      constexpr int n = decltype(N)::value;
-      constexpr int newer = (VSTEPS - 1 - n) < (VPF - 1) ? (VSTEPS - 1 - n) : (VPF - 1);
-      const u32x4_t cur = lgkm_wait_v<2 * newer>(va[n % VPF]);
-      PvMfma<DT>::run(st.o[n % NMT], cur, pf_in[n / NMT]);
-      if constexpr (n + VPF < VSTEPS) va[n % VPF] = v_frag(std::integral_constant<int, n + VPF>{});
-#if PA_MLA_SM_AFTER == 0
-      if constexpr (DO_SM && (n % 2 == 1) && (n / 2 < NCHUNK)) sm_chunk(std::integral_constant<int, n / 2>{});
-      __builtin_amdgcn_sched_barrier(0);
-#endif
-    });
-#if PA_MLA_SM_AFTER
-    if constexpr (DO_SM) static_for<0, NCHUNK>([&](auto C) { sm_chunk(C); });
-#endif
-  } else if constexpr (DO_SM) {
-    static_for<0, NCHUNK>([&](auto C) { sm_chunk(C); });
+  } else if constexpr (C == 1) {
+    // mask and tile max
+    if (full_tile) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sm.tmax = fmaxf(sm.tmax, sm.s[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = key0 + hi * 4 + (e & 3) + 8 * (e >> 2);
+        const float v = (j <= pos && j >= lo_row) ? sm.s[e] : -INFINITY;
+        sm.s[e] = v;
+        sm.tmax = fmaxf(sm.tmax, v);
+      }
+    }
+  } else if constexpr (C == 2) {
+    const float tmax = max_xor32(sm.tmax);
+    st.m_seen = fmaxf(st.m_seen, tmax);
+    if (st.m_ref == -INFINITY) st.m_ref = tmax;
+    st.ovf |= tmax > st.m_ref + PRange<DT>::value;
+    sm.m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
+  } else if constexpr (C >= 3 && C < 11) {
+    constexpr int k = C - 3;   // probabilities of elements 2k, 2k + 1 -> word k of the fragments
+    const float p0 = fast_exp2(sm.s[2 * k] - sm.m_use);
+    const float p1 = fast_exp2(sm.s[2 * k + 1] - sm.m_use);
+    sm.psum += p0 + p1;
+    sm.pf[k >> 2][k & 3] = DT::from_f32(p0) | (DT::from_f32(p1) << 16);
+  } else if constexpr (C == 11) {
+    st.l_run += sm.psum;
   }
+  static_assert(C < kSmChunks, "softmax steps");
+}
+
+// This wave's probabilities to the P buffer at Pb: fragment (row block w,
+// k-step ks) at Pb + (2 w + ks) * 1024, lane-major.
+__device__ __forceinline__ void mla_sm_store(const MlaSm& sm, uint32_t Pb) {
+  const uint32_t dst = Pb + (uint32_t)(threadIdx.x >> 6) * 2048u + (uint32_t)(threadIdx.x & 63) * 16u;
+  ds_write_b128_v<0>(dst, sm.pf[0]);
+  ds_write_b128_v<1024>(dst, sm.pf[1]);
+}
+
+// PV step with the value channels split across the waves: O^T += V^T P^T for
+// the tile at LDS address Lv, where wave w holds all 128 rows of the query
+// tile and value channels [128 w, 128 w + 128). Its A operands are the V^T
+// fragments of its own channel blocks only (transposing reads; the wave's
+// offset is folded into vaddr) and its B operands are the four row blocks'
+// probabilities P^T, which every wave wrote to the P buffer at Lp. Compared
+// with every wave reading all of V for its own 32 rows, a wave reads a
+// quarter of V plus 8 KB of P per tile. k-index 8 g + e of lane group g is
+// key 4 g + (e & 3) + 8 (e >> 2), the key order of the S^T accumulator.
+// between(n) runs after MFMA n (the next tile's softmax steps; the MFMAs leave
+// issue slots for them).
+template <typename DT, int HSP, int VHSP, typename Between>
+__device__ __forceinline__ void mla_pv(MlaState<HSP, VHSP>& st, uint32_t Lv, const uint32_t (&vaddr)[4], uint32_t Lp,
+                                       Between&& between) {
+  constexpr int NMT = VHSP / 32;
+  static_assert(NMT == 16, "four waves x four 32-channel blocks x four row blocks");
+  constexpr int VSTEPS = 32;
+  const uint32_t plane = (uint32_t)(threadIdx.x & 63) * 16u;
+
+  // The registers an LDS read (inline assembly) writes are filled when the
+  // read completes, so nothing may copy them before the lgkmcnt wait that
+  // covers the read: fragments used by several MFMAs are waited for in place
+  // (vf/p0/p1 are the read destinations themselves; the two transposing reads
+  // of a V^T fragment land in the halves of one register tuple), and a
+  // fragment is never rebuilt by VALU moves right before the MFMA that reads
+  // it (an inline-assembly MFMA gets no hazard wait states from the compiler).
+  // V^T fragment (ks, c): 32 channels x 16 keys of this wave's channel block c.
+  u32x4_t vf[4], p0[4], p1[4];
+  auto v_frag = [&](auto KS, auto C) {
+    constexpr int ks = decltype(KS)::value, c = decltype(C)::value;
+    constexpr int off = ks * 16 * MlaLds<HSP>::ROWB + (c >> 1) * 128;
+    const u32x2_t r0 = ds_read_tr16_b64_asm<off>(Lv + vaddr[c & 1]);
+    const u32x2_t r1 = ds_read_tr16_b64_asm<off>(Lv + vaddr[2 + (c & 1)]);
+    vf[c] = u32x4_t{r0[0], r0[1], r1[0], r1[1]};
+  };
+  auto p_frag = [&](auto KS, auto R) -> u32x4_t {
+    constexpr int ks = decltype(KS)::value, r = decltype(R)::value;
+    return ds_read_b128_asm<(2 * r + ks) * 1024>(Lp + plane);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  static_for<0, 4>([&](auto R) { p0[decltype(R)::value] = p_frag(I0{}, R); });
+  v_frag(I0{}, I0{});
+  v_frag(I0{}, I1{});
+  static_for<0, VSTEPS>([&](auto N) {
+    constexpr int n = decltype(N)::value;
+    constexpr int ks = n / 16, c = (n / 4) % 4, r = n % 4;
+    u32x4_t& b = ks == 0 ? p0[r] : p1[r];
+    // Wait where a fragment is first used: V^T(ks, c) at r == 0, P(ks, r)
+    // at c == 0 (later uses find it complete).
+    if constexpr (r == 0 || c == 0)
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vf[c]), "+v"(b) : "n"(PvSched::wait(n)));
+    PvMfma<DT>::run(st.o[4 * c + r], vf[c], b);
+    // Reads issued after this MFMA (PvSched::at).
+    if constexpr (n == 0) v_frag(I0{}, std::integral_constant<int, 2>{});
+    if constexpr (n == 4) v_frag(I0{}, std::integral_constant<int, 3>{});
+    if constexpr (n == 8) {
+      v_frag(I1{}, I0{});
+      p1[0] = p_frag(I1{}, I0{});
+      p1[1] = p_frag(I1{}, I1{});
+    }
+    if constexpr (n == 10) {
+      p1[2] = p_frag(I1{}, std::integral_constant<int, 2>{});
+      p1[3] = p_frag(I1{}, std::integral_constant<int, 3>{});
+    }
+    if constexpr (n == 12) v_frag(I1{}, I1{});
+    if constexpr (n == 16) v_frag(I1{}, std::integral_constant<int, 2>{});
+    if constexpr (n == 20) v_frag(I1{}, std::integral_constant<int, 3>{});
+    between(N);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 template <typename DT, int HSP, int VHSP>
@@ -338,7 +416,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int SLOTS = KW * CPR;         // 16-byte copies per wave per tile
   constexpr int LOADS = SLOTS / 64;       // copy instructions per wave per tile
   constexpr int BUF_BYTES = KT * CPR * 16;
-  constexpr int LDS_BYTES = NB * BUF_BYTES;
+  constexpr int PB_BYTES = 2 * NW * 2 * 1024;   // two P buffers: [2][row block][k-step][64 lanes x 16 B]
+  constexpr int LDS_BYTES = NB * BUF_BYTES + PB_BYTES;
   static_assert(SLOTS % 64 == 0, "whole copy instructions");
   static_assert(HSP % 64 == 0 && VHSP % 32 == 0 && VHSP <= HSP, "head sizes");
   static_assert((NB - 3) * LOADS <= 63, "vmcnt range");
@@ -398,6 +477,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int pos = past_b + tq;
     const int lo_row = p.window >= 0 ? max(0, pos - p.window) : 0;
     const int64_t qrow = (int64_t)(cum_b + tq) * p.H + h;
+    // Wave-uniform visibility bounds over the wave's valid rows: a tile with
+    // lo_max <= first key and last key <= pos_min needs no masking.
+    int pos_min = row_ok ? pos : INT_MAX, lo_max = row_ok ? lo_row : INT_MIN;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      pos_min = min(pos_min, __shfl_xor(pos_min, d));
+      lo_max = max(lo_max, __shfl_xor(lo_max, d));
+    }
+    pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+    lo_max = __builtin_amdgcn_readfirstlane(lo_max);
+    auto tile_full = [&](int key0) { return key0 >= lo_max && key0 + KT - 1 <= pos_min; };
 
     // Query fragments: k-step s holds channels 16 s + 8 hi .. + 8 of the row.
     // The wave's 32 rows are consecutive in `query`; one wave-uniform buffer
@@ -448,40 +538,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       return ld_uniform(p.bt + (int64_t)b * p.MB + min(kw0 >> p.bs_log2, p.MB - 1));
     };
     // A planned tile copy: descriptor over the wave's KW cache rows, LDS
-    // destination, and whether every key of the slice is in range.
+    // destination. Keys at or past kv_hi (and every key of a tile past the
+    // piece) lie past the descriptor's range and land as zeros, so the only
+    // per-lane masking left is for keys below kv_lo (`lower`, rare: the first
+    // tile of a piece whose range does not start on a tile boundary).
     struct CopyPlan {
       u32x4_t rsrc;
       uint32_t dst0;
       int kw0;
-      bool full;
+      bool lower;
     };
     auto plan = [&](int tile, int bufi, int blk_raw) -> CopyPlan {
       CopyPlan c;
       c.kw0 = tile * KT + w * KW;
       const int blk = clamp_block(blk_raw, p.nblk);
       const uint16_t* rows = p.cache + (((int64_t)blk << p.bs_log2) + (c.kw0 & ((1 << p.bs_log2) - 1))) * p.hs;
-      c.rsrc = rsrc_words_u(rows, (uint32_t)(KW * p.hs * 2));
+      const int nkeys = tile < tile_b ? min(max(t.kv_hi - c.kw0, 0), KW) : 0;
+      c.rsrc = rsrc_words_u(rows, (uint32_t)(nkeys * p.hs * 2));
       c.dst0 = lds_addr(lds_raw) + (uint32_t)(bufi * BUF_BYTES + w * SLOTS * 16);
-      c.full = c.kw0 >= t.kv_lo && c.kw0 + KW <= t.kv_hi;
+      c.lower = tile < tile_b && c.kw0 < t.kv_lo;
       return c;
     };
     // Copy instruction `it` of a planned tile (LDS slots it*64 .. it*64+63 of
     // the wave's slice). Exactly LOADS of them per tile and wave (vmcnt counts
-    // them).
-    auto copy_one = [&](const CopyPlan& c, int it) {
+    // them). LOWER: keys below kv_lo take an out-of-range offset.
+    auto copy_one = [&](const CopyPlan& c, int it, auto LOWER) {
       uint32_t o2 = load_off2[it >> 1];
       asm volatile("" : "+v"(o2));
-      uint32_t off = (o2 >> ((it & 1) * 16)) & 0xFFFFu;
-      if (!c.full) {
+      uint32_t off = (it & 1) ? (o2 >> 16) : (o2 & 0xFFFFu);
+      if constexpr (decltype(LOWER)::value) {
         const int j = c.kw0 + (it * 64 + opaque_lane()) / CPR;
-        off = (j >= t.kv_lo && j < t.kv_hi) ? off : kOutOfRange;
+        off = j >= t.kv_lo ? off : kOutOfRange;
       }
       copy16_to_lds(c.dst0 + it * 64 * 16, off, c.rsrc);
     };
     auto issue = [&](int tile, int bufi, int blk_raw) {
       const CopyPlan c = plan(tile, bufi, blk_raw);
+      if (c.lower) {
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) copy_one(c, it);
+        for (int it = 0; it < LOADS; ++it) copy_one(c, it, std::true_type{});
+      } else {
+#pragma unroll
+        for (int it = 0; it < LOADS; ++it) copy_one(c, it, std::false_type{});
+      }
     };
 
     // LDS fragment addresses of this lane relative to a tile buffer.
@@ -500,12 +599,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int sw0 = mla_swizzle(k0b), sw1 = mla_swizzle(k0b + 8);
       const int lcb = 2 * (g & 1) + (cq >> 1);
 #pragma unroll
+      // This wave's value channels start at chunk 16 w (byte 256 w of the row;
+      // the swizzle only permutes chunks within aligned groups of 8).
       for (int par = 0; par < 2; ++par) {
-        vaddr[par] = k0b * CPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
-        vaddr[2 + par] = (k0b + 8) * CPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
+        vaddr[par] = k0b * CPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8 + 256 * w;
+        vaddr[2 + par] = (k0b + 8) * CPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8 + 256 * w;
       }
     }
     const uint32_t lds0 = lds_addr(lds_raw);
+    // P buffer of tile k: pbuf0 + ((k - tile_a) & 1) * (PB_BYTES / 2).
+    const uint32_t pbuf0 = lds0 + NB * BUF_BYTES;
 
     // One pass normally; a second one (reference = the rows' exact maxima from
     // the first) only when some score overflowed the first pass's reference.
@@ -519,9 +622,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // and tt + 2 are in flight; tt + 2 reuses the buffer of tt - 2, whose V
       // every wave consumed before this iteration's barrier.
       constexpr int AHEAD = NB - 2;   // tiles in flight beyond the current one
+      // Every iteration issues the copies of one tile (empty past the piece),
+      // so the copy wait below is the same on every tile.
 #pragma unroll
-      for (int k = 0; k < AHEAD; ++k)
-        if (tile_a + k < tile_b) issue(tile_a + k, k, block_of(tile_a + k));
+      for (int k = 0; k < AHEAD; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
       {
         const u32x4_t z = {0u, 0u, 0u, 0u};
         asm volatile("s_nop 4");   // VALU write of z precedes its use as SrcA/B
@@ -535,37 +639,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int rpos = row_ok ? pos : -1;
       // One pipeline step: wait for tile tt, queue QK(tt) with the copies of
       // tile tt + AHEAD, then (PV(tt - 1) and) the softmax of tt.
-      auto qk_step = [&](int tt) -> f32x16_t {
-        vm_wait_tiles<LOADS, AHEAD - 1>(min(AHEAD - 1, tile_b - 1 - tt));
+      auto qk_step = [&](int tt, auto&& between) -> f32x16_t {
+        static_assert(AHEAD == 2, "one tile of copies in flight beyond tile tt");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
         lds_barrier();   // tile tt complete; every wave is done with tile tt - 2
         // Copies of tile tt + AHEAD go out during the QK MFMAs of tile tt; their
         // block id was read one iteration earlier.
         const int blk_cur = blk_next;
         blk_next = block_of(min(tt + AHEAD + 1, tile_b - 1));
-        const bool more = tt + AHEAD < tile_b;
-        const CopyPlan cp = plan(tt + AHEAD, (tt + AHEAD - tile_a) % NB, blk_cur);
-        return mla_qk<DT, HSP, LOADS>(st.qf, lds0 + ((tt - tile_a) % NB) * BUF_BYTES, kaddr, [&](auto IT) {
-          if (more) copy_one(cp, decltype(IT)::value);
-        });
+        const CopyPlan cp = plan(tt + AHEAD, (uint32_t)(tt + AHEAD - tile_a) & (NB - 1), blk_cur);
+        const uint32_t L = lds0 + ((uint32_t)(tt - tile_a) & (NB - 1)) * BUF_BYTES;
+        if (cp.lower)
+          return mla_qk<DT, HSP, LOADS>(
+              st.qf, L, kaddr, [&](auto IT) { copy_one(cp, decltype(IT)::value, std::true_type{}); }, between);
+        return mla_qk<DT, HSP, LOADS>(
+            st.qf, L, kaddr, [&](auto IT) { copy_one(cp, decltype(IT)::value, std::false_type{}); }, between);
       };
-      u32x4_t pf[2];
+      // Iteration tt: QK(tt), then PV(tt - 1) with the softmax of tt between
+      // its MFMAs (step c after PV MFMA 2 c + 1); P(tt) goes to the P buffer
+      // of tt's parity. PV(tt - 1) reads P(tt - 1), which every wave wrote
+      // before this iteration's first barrier; the buffer P(tt) overwrites
+      // was last read by PV(tt - 2), before that barrier too.
+      auto tile_lds = [&](int tt) -> uint32_t { return lds0 + ((uint32_t)(tt - tile_a) & (NB - 1)) * BUF_BYTES; };
+      auto pbuf = [&](int tt) -> uint32_t { return pbuf0 + ((uint32_t)(tt - tile_a) & 1) * (PB_BYTES / 2); };
+      auto noop = [](auto) {};
       {
-        const f32x16_t sacc = qk_step(tile_a);
-        mla_pv_softmax<DT, HSP, VHSP, false, true>(st, 0, vaddr, pf, sacc, tile_a * KT, rpos, lo_row, softcap_on, p,
-                                                   pf);
+        MlaSm sm;
+        sm.s = qk_step(tile_a, noop);
+        static_for<0, kSmChunks>([&](auto C) {
+          mla_sm_chunk<DT, HSP, VHSP, decltype(C)::value>(st, sm, tile_a * KT, rpos, lo_row, tile_full(tile_a * KT),
+                                                          softcap_on, p);
+        });
+        mla_sm_store(sm, pbuf(tile_a));
       }
       for (int tt = tile_a + 1; tt < tile_b; ++tt) {
-        const f32x16_t sacc = qk_step(tt);
-        const uint32_t Lv = lds0 + ((tt - 1 - tile_a) % NB) * BUF_BYTES;
-        u32x4_t pf_new[2];
-        mla_pv_softmax<DT, HSP, VHSP, true, true>(st, Lv, vaddr, pf, sacc, tt * KT, rpos, lo_row, softcap_on, p,
-                                                  pf_new);
-        pf[0] = pf_new[0];
-        pf[1] = pf_new[1];
+        MlaSm sm;
+        sm.s = qk_step(tt, noop);
+        const int key0 = tt * KT;
+        const bool full = tile_full(key0);
+        mla_pv<DT, HSP, VHSP>(st, tile_lds(tt - 1), vaddr, pbuf(tt - 1), [&](auto N) {
+          constexpr int n = decltype(N)::value;
+          if constexpr (n % 2 == 1 && n / 2 < kSmChunks)
+            mla_sm_chunk<DT, HSP, VHSP, n / 2>(st, sm, key0, rpos, lo_row, full, softcap_on, p);
+        });
+        mla_sm_store(sm, pbuf(tt));
       }
-      // PV of the last tile (its buffer is still resident).
-      mla_pv_softmax<DT, HSP, VHSP, true, false>(st, lds0 + ((tile_b - 1 - tile_a) % NB) * BUF_BYTES, vaddr, pf,
-                                                 f32x16_t{}, 0, 0, 0, false, p, pf);
+      // PV of the last tile (its buffer is still resident) once every wave's
+      // P of that tile is in LDS.
+      lds_barrier();
+      mla_pv<DT, HSP, VHSP>(st, tile_lds(tile_b - 1), vaddr, pbuf(tile_b - 1), noop);
+      // The last copies (tiles past the piece, zero-filled) land before the
+      // tile buffers are reused below.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       // Whole-workgroup vote on a second pass (the tile buffers are free once
       // every wave passed the barrier; the flags sit in the first buffer).
       lds_barrier();
@@ -581,16 +706,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // Epilogue through LDS (the tile buffers are free): O^T of all rows is
-    // staged as float32 rows, half of the value channels at a time, written
-    // straight from the accumulation registers, then every thread normalises
-    // (whole tile) or copies (partial result) 8 consecutive channels of a row
-    // with coalesced stores. Rows are padded by 16 bytes against bank conflicts.
+    // staged as float32 rows in two rounds, round k holding channel blocks
+    // 2k, 2k + 1 of every wave (wave w's 64 channels at staged column 64 w),
+    // written straight from the accumulation registers; then every thread
+    // normalises (whole tile) or copies (partial result) 8 consecutive
+    // channels of a row with coalesced stores. Rows are padded by 16 bytes
+    // against bank conflicts.
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    constexpr int HALF = VHSP / 2;
-    constexpr int ORS = HALF + 4;                          // floats per staged row
-    constexpr int C8 = HALF / 8;                           // 8-channel groups per staged row
-    static_assert((RW * ORS + 2 * RW) * 4 <= LDS_BYTES, "epilogue staging fits the tile buffers");
-    static_assert((NMT / 2) % 1 == 0 && HALF % 32 == 0, "whole accumulator blocks per half");
+    constexpr int QCH = VHSP / NW;                         // value channels per wave
+    constexpr int RCH = QCH / 2;                           // per wave and round
+    constexpr int SCOL = NW * RCH;                         // staged columns per round
+    constexpr int ORS = SCOL + 4;                          // floats per staged row
+    constexpr int C8 = SCOL / 8;                           // 8-channel groups per staged row
+    static_assert((RW * ORS + 2 * RW) * 4 <= NB * BUF_BYTES, "epilogue staging fits the tile buffers");
+    static_assert(RCH == 64, "two 32-channel blocks per wave and round");
     float* const ost = (float*)lds_raw;
     float* const rowl = ost + RW * ORS;                    // [RW] denominators
     if (hi == 0) rowl[rloc] = l_tot;
@@ -600,25 +729,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       ml[0] = st.m_ref;
       ml[1] = l_tot;
     }
-    const uint32_t wbase = lds_addr(ost) + (uint32_t)((rloc * ORS + 4 * hi) * 4);
+    // Lane's staging address for row block r: row 32 r + l32, column 64 w + 4 hi.
+    uint32_t wb[NW];
+#pragma unroll
+    for (int r = 0; r < NW; ++r) wb[r] = lds_addr(ost) + (uint32_t)(((32 * r + l32) * ORS + RCH * w + 4 * hi) * 4);
     const int64_t orow0 = (int64_t)cum_b * p.H + t.row0;  // output row of local row 0
-    static_for<0, 2>([&](auto HF) {
-      constexpr int half = decltype(HF)::value;
-      static_for<0, 2 * NMT>([&](auto K) {
-        constexpr int mloc = decltype(K)::value / 4;
-        constexpr int j = decltype(K)::value % 4;
-        constexpr int mt = half * (NMT / 2) + mloc;
-        const f32x4_t part = __builtin_shufflevector(st.o[mt], st.o[mt], 4 * j, 4 * j + 1, 4 * j + 2, 4 * j + 3);
-        ds_write_b128_acc<(32 * mloc + 8 * j) * 4>(wbase, part);
+    static_for<0, 2>([&](auto RD) {
+      constexpr int rd = decltype(RD)::value;
+      static_for<0, 2 * NW * 4>([&](auto K) {
+        constexpr int kk = decltype(K)::value;
+        constexpr int cl = kk / (NW * 4), r = (kk / 4) % NW, j = kk % 4;
+        constexpr int c = 2 * rd + cl;
+        const f32x4_t part = __builtin_shufflevector(st.o[4 * c + r], st.o[4 * c + r], 4 * j, 4 * j + 1, 4 * j + 2,
+                                                     4 * j + 3);
+        ds_write_b128_acc<(32 * cl + 8 * j) * 4>(wb[r], part);
       });
-      lds_barrier();     // staged half visible (the asm writes are waited for by lgkmcnt(0))
+      lds_barrier();     // staged round visible (the asm writes are waited for by lgkmcnt(0))
       for (int idx = (int)threadIdx.x; idx < RW * C8; idx += NW * 64) {
         const int r = idx / C8;
-        const int c = (idx - r * C8) * 8;
-        const int cg = half * HALF + c;                    // value channel
+        const int sc = (idx - r * C8) * 8;                 // staged column
+        const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);   // value channel
         if (r >= t.nrows || cg >= p.vhs) continue;
-        const f32x4_t v0 = *(const f32x4_t*)(ost + r * ORS + c);
-        const f32x4_t v1 = *(const f32x4_t*)(ost + r * ORS + c + 4);
+        const f32x4_t v0 = *(const f32x4_t*)(ost + r * ORS + sc);
+        const f32x4_t v1 = *(const f32x4_t*)(ost + r * ORS + sc + 4);
         if (whole) {
           const float lr = rowl[r];
           const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
