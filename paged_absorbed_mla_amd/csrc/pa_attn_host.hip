@@ -38,14 +38,17 @@ struct SchedParams {
   uint32_t* zero16;
 };
 
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 256;
 
 // Exclusive prefix sum over n values get(i), written with put(i, prefix);
-// returns the total. Every thread of the block must call it.
+// returns the total. Every thread of the block must call it. Per chunk of
+// kSchedThreads values: a shuffle scan inside each wave, then every thread
+// adds the totals of the waves before its own (read from LDS in parallel, no
+// serial pass).
 template <typename Get, typename Put>
 __device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
-  __shared__ int64_t wave_sums[kSchedThreads / 64];
-  __shared__ int64_t chunk_total;
+  constexpr int NWV = kSchedThreads / 64;
+  __shared__ int64_t wave_sums[NWV];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t carry = 0;
   for (int64_t base = 0; base < n; base += kSchedThreads) {
@@ -59,18 +62,15 @@ __device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
     }
     if (lane == 63) wave_sums[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int64_t run = 0;
-      for (int k = 0; k < kSchedThreads / 64; ++k) {
-        const int64_t s = wave_sums[k];
-        wave_sums[k] = run;
-        run += s;
-      }
-      chunk_total = run;
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) {
+      const int64_t ws = wave_sums[k];
+      before += k < wave ? ws : 0;
+      total += ws;
     }
-    __syncthreads();
-    if (idx < n) put(idx, carry + wave_sums[wave] + x - v);
-    carry += chunk_total;
+    if (idx < n) put(idx, carry + before + x - v);
+    carry += total;
     __syncthreads();
   }
   return carry;
@@ -107,14 +107,161 @@ __device__ void query_rope_chunk(const SchedParams& p, int64_t idx, const int32_
   *(u32x4_t*)(p.qrot + row * p.rd + (c0 - p.ro)) = pack8<DT>(x);
 }
 
-// Block 0 keeps its working arrays (sequence bounds, per-tile unit counts and
-// prefix sums, workgroup ranges) in LDS, so each dependent step (scans and
-// binary searches) costs LDS latency instead of a global round trip; larger
-// problems fall back to the same arrays in the workspace.
+// Block 0 of the schedule launch builds the whole schedule in working arrays
+// and writes its outputs (tile table, workgroup ranges, header) only at the
+// end: a global store inside the build would make every later barrier wait
+// for its write to complete. The arrays live in LDS when they fit (then the
+// build runs on LDS instructions: IN_LDS is a template argument, so the
+// compiler sees the LDS array itself), else in the workspace.
 constexpr int kSchedLdsInts = 12288;
 
-__device__ __forceinline__ int64_t sched_ints(int B, int64_t max_mtiles, int grid) {
-  return 3 * (int64_t)B + 2 + 2 * max_mtiles + 1 + grid + 1;
+__host__ __device__ inline int64_t sched_ints(int B, int64_t max_mtiles, int grid) {
+  return 3 * (int64_t)B + 2 + 7 * max_mtiles + 1 + 2 * (int64_t)grid + 1;
+}
+
+template <bool IN_LDS>
+__device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* lds_arr) {
+  int32_t* const base = IN_LDS ? lds_arr : p.sched;
+  int32_t* const cum = base;                           // [B + 1] cumulative_sequence_length
+  int32_t* const pst = cum + (p.B + 1);                // [B] past lengths (negative -> 0)
+  int32_t* const sbase = pst + p.B;                    // [B + 1] first query tile of each sequence
+  int32_t* const u0 = sbase + (p.B + 1);               // [max_mtiles + 1] KV tiles, then first unit
+  int32_t* const np = u0 + (p.max_mtiles + 1);        // [max_mtiles] workgroups per query tile
+  int32_t* const tb = np + p.max_mtiles;               // [max_mtiles] sequence of each tile
+  int32_t* const trow = tb + p.max_mtiles;             // [max_mtiles] first row, then rows (2 x)
+  int32_t* const tkv = trow + 2 * p.max_mtiles;        // [max_mtiles] kv_lo, kv_hi (2 x)
+  int32_t* const wr = tkv + 2 * p.max_mtiles;          // [grid + 1] unit range of every workgroup
+  int32_t* const wt = wr + (p.grid + 1);               // [grid] query tile of every workgroup
+
+  for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
+    cum[b] = p.cumseq[b];
+    if (b < p.B) pst[b] = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
+  }
+  __syncthreads();
+  // A. query tiles per sequence, prefix-summed into sbase.
+  const int64_t M_all = block_exclusive_scan(
+      p.B,
+      [&](int64_t b) -> int64_t {
+        const int64_t rows = (int64_t)(cum[b + 1] - cum[b]) * p.H;
+        return (rows + p.RW - 1) / p.RW;
+      },
+      [&](int64_t b, int64_t v) { sbase[b] = (int32_t)v; });
+  // M cannot exceed max_mtiles when cumseq[B] = T (a precondition); clamp so a
+  // violated precondition cannot write past the tile table.
+  const int M = (int)min(M_all, p.max_mtiles);
+  if (threadIdx.x == 0) sbase[p.B] = (int32_t)M_all;
+  __syncthreads();
+  // B. describe every query tile; its KV tile count goes to u0 for now.
+  for (int i = threadIdx.x; i < M; i += kSchedThreads) {
+    int lo = 0, hi = p.B - 1;  // last b with sbase[b] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sbase[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int rows = (cum[b + 1] - cum[b]) * p.H;
+    const int row0 = (i - sbase[b]) * p.RW;
+    const int nrows = min(p.RW, rows - row0);
+    const int pos0 = pst[b] + row0 / p.H;
+    const int pos1 = pst[b] + (row0 + nrows - 1) / p.H;
+    const int kv_hi = pos1 + 1;
+    const int kv_lo = p.window >= 0 ? max(0, pos0 - p.window) : 0;
+    tb[i] = b;
+    trow[2 * i] = row0;
+    trow[2 * i + 1] = nrows;
+    tkv[2 * i] = kv_lo;
+    tkv[2 * i + 1] = kv_hi;
+    u0[i] = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
+  }
+  __syncthreads();
+  // C. units: prefix sum of KV tiles.
+  const int64_t U = block_exclusive_scan(
+      M, [&](int64_t i) -> int64_t { return u0[i]; }, [&](int64_t i, int64_t v) { u0[i] = (int32_t)v; });
+  if (threadIdx.x == 0) u0[M] = (int32_t)U;
+  __syncthreads();
+  // D. unit range of every workgroup. Split-KV: the units are laid out with
+  // piece_units virtual units before each query tile (the cost of the query
+  // load and epilogue a piece adds), and the virtual line is cut evenly; a
+  // workgroup that enters a second query tile thus takes fewer KV tiles. A
+  // cut inside a tile's virtual prefix falls on the tile's first unit.
+  // Empty ranges sit only at the end or right before a tile's first
+  // workgroup, so the workgroups that share a query tile are consecutive and
+  // each of them writes its partial slot.
+  const int64_t alpha = p.piece_units;
+  const int64_t Uv = U + alpha * M;
+  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
+    int32_t v;
+    if (!p.split_kv) {
+      v = u0[min(w, M)];
+    } else if (M == 0) {
+      v = 0;
+    } else {
+      const int64_t x = Uv >= p.grid ? ((int64_t)w * Uv) / p.grid : min((int64_t)w, Uv);
+      int lo = 0, hi = M - 1;   // last tile whose virtual start is <= x
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (u0[mid] + alpha * mid <= x) lo = mid; else hi = mid - 1;
+      }
+      const int64_t o = x - (u0[lo] + alpha * lo);
+      v = (int32_t)min(u0[lo] + max(o - alpha, (int64_t)0), (int64_t)u0[lo + 1]);
+    }
+    wr[w] = v;
+  }
+  __syncthreads();
+  // E. pieces per query tile, and the query tile holding each workgroup's
+  // first unit (the last i with u0[i] <= wr[w]).
+  for (int i = threadIdx.x; i < M; i += kSchedThreads) {
+    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
+    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
+    np[i] = w1 - w0 + 1;
+  }
+  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
+    const int uw = wr[w];
+    int lo = 0, hi = M > 0 ? M - 1 : 0;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (u0[mid] <= uw) lo = mid; else hi = mid - 1;
+    }
+    wt[w] = lo;
+  }
+  __syncthreads();
+  // F. partial slots for the tiles that several workgroups share; np[i]
+  // becomes the tile's first slot (-1: one workgroup, no partial results).
+  const int64_t slots = block_exclusive_scan(
+      M, [&](int64_t i) -> int64_t { const int n = np[i]; return n > 1 ? n : 0; },
+      [&](int64_t i, int64_t v) { np[i] = np[i] > 1 ? (int32_t)v : -1; });
+  __syncthreads();
+  // Outputs, all stores at the end.
+  if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < M; i += kSchedThreads) {
+    MTile t;
+    t.b = tb[i];
+    t.row0 = trow[2 * i];
+    t.nrows = trow[2 * i + 1];
+    t.kv_lo = tkv[2 * i];
+    t.kv_hi = tkv[2 * i + 1];
+    t.unit0 = u0[i];
+    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
+    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
+    t.w_first = w0;
+    t.npieces = w1 - w0 + 1;
+    t.part_base = np[i];
+    t.pad[0] = t.pad[1] = t.pad[2] = 0;
+    p.mt[i] = t;
+  }
+  if (threadIdx.x == 0) {
+    MTile t = {};
+    t.unit0 = (int32_t)U;
+    p.mt[M] = t;
+    p.header[0] = (int32_t)U;
+    p.header[1] = M;
+    p.header[2] = (int32_t)slots;
+    p.header[3] = (slots > p.part_cap || M_all > p.max_mtiles) ? 1 : 0;
+  }
+  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
+    p.wg_range[w] = wr[w];
+    if (w < p.grid) p.wg_tile[w] = wt[w];
+  }
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
@@ -140,128 +287,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     }
     return;
   }
-  const bool in_lds = sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts;
-  int32_t* const base = in_lds ? lds_arr : p.sched;
-  int32_t* const cum = base;                           // [B + 1] cumulative_sequence_length
-  int32_t* const pst = cum + (p.B + 1);                // [B] past lengths (negative -> 0)
-  int32_t* const sbase = pst + p.B;                    // [B + 1] first query tile of each sequence
-  int32_t* const u0 = sbase + (p.B + 1);               // [max_mtiles + 1] KV tiles, then first unit
-  int32_t* const np = u0 + (p.max_mtiles + 1);        // [max_mtiles] workgroups per query tile
-  int32_t* const wr = np + p.max_mtiles;               // [grid + 1] unit range of every workgroup
-
-  if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
-  for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
-    cum[b] = p.cumseq[b];
-    if (b < p.B) pst[b] = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
-  }
-  __syncthreads();
-  // A. query tiles per sequence, prefix-summed into sbase.
-  const int64_t M_all = block_exclusive_scan(
-      p.B,
-      [&](int64_t b) -> int64_t {
-        const int64_t rows = (int64_t)(cum[b + 1] - cum[b]) * p.H;
-        return (rows + p.RW - 1) / p.RW;
-      },
-      [&](int64_t b, int64_t v) { sbase[b] = (int32_t)v; });
-  // M cannot exceed max_mtiles when cumseq[B] = T (a precondition); clamp so a
-  // violated precondition cannot write past the tile table.
-  const int64_t M = min(M_all, p.max_mtiles);
-  if (threadIdx.x == 0) sbase[p.B] = (int32_t)M_all;
-  __syncthreads();
-  // B. describe every query tile; its KV tile count goes to u0 for now.
-  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
-    int lo = 0, hi = p.B - 1;  // last b with sbase[b] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sbase[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int rows = (cum[b + 1] - cum[b]) * p.H;
-    const int row0 = (int)(i - sbase[b]) * p.RW;
-    const int nrows = min(p.RW, rows - row0);
-    const int pos0 = pst[b] + row0 / p.H;
-    const int pos1 = pst[b] + (row0 + nrows - 1) / p.H;
-    const int kv_hi = pos1 + 1;
-    const int kv_lo = p.window >= 0 ? max(0, pos0 - p.window) : 0;
-    MTile* t = p.mt + i;
-    t->b = b;
-    t->row0 = row0;
-    t->nrows = nrows;
-    t->kv_lo = kv_lo;
-    t->kv_hi = kv_hi;
-    u0[i] = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
-  }
-  __syncthreads();
-  // C. units: prefix sum of KV tiles.
-  const int64_t U = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { return u0[i]; }, [&](int64_t i, int64_t v) { u0[i] = (int32_t)v; });
-  if (threadIdx.x == 0) u0[M] = (int32_t)U;
-  __syncthreads();
-  // D. unit range of every workgroup. Split-KV: the units are laid out with
-  // piece_units virtual units before each query tile (the cost of the query
-  // load and epilogue a piece adds), and the virtual line is cut evenly; a
-  // workgroup that enters a second query tile thus takes fewer KV tiles. A
-  // cut inside a tile's virtual prefix falls on the tile's first unit.
-  // Empty ranges sit only at the end or right before a tile's first
-  // workgroup, so the workgroups that share a query tile are consecutive and
-  // each of them writes its partial slot.
-  const int64_t alpha = p.piece_units;
-  const int64_t Uv = U + alpha * M;
-  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
-    int32_t v;
-    if (!p.split_kv) {
-      v = u0[min((int64_t)w, M)];
-    } else if (M == 0) {
-      v = 0;
-    } else {
-      const int64_t x = Uv >= p.grid ? ((int64_t)w * Uv) / p.grid : min((int64_t)w, Uv);
-      int64_t lo = 0, hi = M - 1;   // last tile whose virtual start is <= x
-      while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (u0[mid] + alpha * mid <= x) lo = mid; else hi = mid - 1;
-      }
-      const int64_t o = x - (u0[lo] + alpha * lo);
-      v = (int32_t)min(u0[lo] + max(o - alpha, (int64_t)0), (int64_t)u0[lo + 1]);
-    }
-    wr[w] = v;
-    p.wg_range[w] = v;
-  }
-  __syncthreads();
-  // E. pieces per query tile, and the query tile holding each workgroup's
-  // first unit (the last i with u0[i] <= wr[w]).
-  for (int64_t i = threadIdx.x; i < M; i += kSchedThreads) {
-    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
-    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
-    np[i] = w1 - w0 + 1;
-    p.mt[i].unit0 = u0[i];
-    p.mt[i].w_first = w0;
-    p.mt[i].npieces = w1 - w0 + 1;
-  }
-  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
-    const int uw = wr[w];
-    int64_t lo = 0, hi = M > 0 ? M - 1 : 0;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (u0[mid] <= uw) lo = mid; else hi = mid - 1;
-    }
-    p.wg_tile[w] = (int32_t)lo;
-  }
-  if (threadIdx.x == 0) {
-    MTile s = {};
-    s.unit0 = (int32_t)U;
-    p.mt[M] = s;
-  }
-  __syncthreads();
-  // F. partial slots for the tiles that several workgroups share.
-  const int64_t slots = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { const int n = np[i]; return n > 1 ? n : 0; },
-      [&](int64_t i, int64_t v) { p.mt[i].part_base = np[i] > 1 ? (int32_t)v : -1; });
-  if (threadIdx.x == 0) {
-    p.header[0] = (int32_t)U;
-    p.header[1] = (int32_t)M;
-    p.header[2] = (int32_t)slots;
-    p.header[3] = (slots > p.part_cap || M > p.max_mtiles) ? 1 : 0;
-  }
+  if (sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts) schedule_build<true>(p, lds_arr);
+  else schedule_build<false>(p, lds_arr);
 }
 
 // ---------------------------------------------------------------------------
@@ -354,7 +381,7 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_zero = off; off = align256(off + 16);
   L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
   L.off_wg_tile = off; off = align256(off + (size_t)L.ranges * sizeof(int32_t));
-  L.sched_ints = 3 * g.B + 2 + 2 * L.max_mtiles + 1 + L.ranges + 1;
+  L.sched_ints = sched_ints(g.B, L.max_mtiles, L.ranges);
   L.off_sched = off; off = align256(off + (size_t)L.sched_ints * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
