@@ -649,9 +649,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 // Grid: (query tiles, RW / kCombineRows) of 256 threads. TPR threads share a
 // row; thread j of a row owns the 4-channel groups j, j + TPR, j + 2 TPR, ...
 // (so each load instruction covers contiguous bytes of a row). Every thread forms its row's
-// weights itself from the (m, l) pairs (read 8 pieces at a time, so the loads
-// overlap), then accumulates the pieces' slices 4 pieces at a time with all
-// their 16-byte loads in flight together (coalesced across the row's threads).
+// weights itself from the (m, l) pairs. Up to QA pieces: the pairs and all
+// slice loads go out together (one round trip). More pieces: the pairs are
+// read 8 pieces at a time, then the slices 4 pieces at a time with all their
+// 16-byte loads in flight together (coalesced across the row's threads).
 constexpr int kCombineRows = 16;
 
 template <typename DT, int VHSP, int RW>
@@ -677,8 +678,41 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     const int c0 = (threadIdx.x % TPR) * 4;                 // channel of group 0; group v at c0 + 4 TPR v
     if (c0 >= p.vhs) continue;
     const float* ml = p.part_ml + ((int64_t)t.part_base * RW + r) * 2;   // piece q at + q * RW * 2
-    // Reference max and denominator: one batch of (m, l) loads per QM pieces
-    // (the usual case, nq <= QM, is a single round trip).
+    const float* pa0 = p.part_acc + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;   // piece q at + q * part_slot
+    f32x4_t acc[NV];
+    if (nq <= QA) {
+      // Up to QA pieces (the usual case): the (m, l) pairs and every slice
+      // load are issued together, one memory round trip per row.
+      f32x4_t a[QA][NV];
+      float m[QA], l[QA];
+#pragma unroll
+      for (int k = 0; k < QA; ++k) {
+        const bool ok = k < nq;
+        const int q = ok ? k : 0;
+        m[k] = ok ? ml[(int64_t)q * RW * 2] : -INFINITY;
+        l[k] = ok ? ml[(int64_t)q * RW * 2 + 1] : 0.0f;
+        const f32x4_t* src = (const f32x4_t*)(pa0 + (int64_t)q * p.part_slot);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) a[k][v] = ok ? src[v * TPR] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < QA; ++k) mx = fmaxf(mx, m[k]);
+      float wq[QA], den = 0.0f;
+#pragma unroll
+      for (int k = 0; k < QA; ++k) {
+        wq[k] = m[k] == -INFINITY ? 0.0f : fast_exp2(m[k] - mx);
+        den += wq[k] * l[k];
+      }
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < QA; ++k)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += (wq[k] * inv) * a[k][v];
+    } else {
+    // Reference max and denominator: one batch of (m, l) loads per QM pieces.
     float mx = -INFINITY, den = 0.0f;
     for (int q0 = 0; q0 < nq; q0 += QM) {
       float m[QM], l[QM];
@@ -699,10 +733,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     // Weighted sum of the row slices.
-    f32x4_t acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float* pa0 = p.part_acc + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;   // piece q at + q * part_slot
     for (int q0 = 0; q0 < nq; q0 += QA) {
       f32x4_t a[QA][NV];
       float wq[QA];
@@ -720,6 +752,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       for (int k = 0; k < QA; ++k)
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] += wq[k] * a[k][v];
+    }
     }
     uint16_t* orow = p.out + ((int64_t)cum_b * p.H + t.row0 + r) * p.vhs + c0;
 #pragma unroll

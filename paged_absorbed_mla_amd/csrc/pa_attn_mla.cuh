@@ -40,6 +40,9 @@ namespace pa {
 #ifndef PA_MLA_QPF
 #define PA_MLA_QPF 4
 #endif
+#ifndef PA_MLA_EPI_FAST
+#define PA_MLA_EPI_FAST 0
+#endif
 #ifndef PA_MLA_VPF
 #define PA_MLA_VPF 3
 #endif
@@ -489,47 +492,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lo_max = __builtin_amdgcn_readfirstlane(lo_max);
     auto tile_full = [&](int key0) { return key0 >= lo_max && key0 + KT - 1 <= pos_min; };
 
-    // Query fragments: k-step s holds channels 16 s + 8 hi .. + 8 of the row.
-    // The wave's 32 rows are consecutive in `query`; one wave-uniform buffer
-    // descriptor starts at its first row and each lane's row and chunk go in
-    // the per-lane offset (chunks past hs take an out-of-range offset and read
-    // zeros).
-    MlaState<HSP, VHSP> st;
-    const int64_t wrow0 = (int64_t)cum_b * p.H + t.row0 + 32 * w;   // first query row of the wave
-    {
-      const u32x4_t qrs = rsrc_words_u(p.query + wrow0 * p.hs, (uint32_t)(32 * p.hs * 2));
-      const int ln = opaque_lane();
-      const int lr = (32 * w + (ln & 31)) < t.nrows ? (ln & 31) : 0;
-      const uint32_t qbase = (uint32_t)(lr * p.hs * 2);
-      const int h8 = (ln >> 5) * 8;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int c0 = 16 * s + h8;
-        st.qf[s] = buffer_load_b128(qrs, c0 < p.hs ? qbase + (uint32_t)(c0 * 2) : kOutOfRange);
-      }
-      // Rotary chunks come from the RoPE'd copy the schedule launch wrote
-      // (qrot, rd channels per row); the test on the k-step is uniform and the
-      // geometry is opaque so nothing is hoisted out of the piece loop.
-      if (p.do_rotary) {
-        int ro = p.ro, rd = p.rd;
-        asm volatile("" : "+s"(ro), "+s"(rd));
-        const u32x4_t rrs = rsrc_words_u(p.qrot + wrow0 * rd, (uint32_t)(32 * rd * 2));
-        const uint32_t rbase = (uint32_t)(lr * rd * 2);
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          if (16 * s + 16 > ro && 16 * s < ro + rd) {
-            const int c0 = 16 * s + h8;
-            if (c0 >= ro && c0 < ro + rd) st.qf[s] = buffer_load_b128(rrs, rbase + (uint32_t)((c0 - ro) * 2));
-          }
-        }
-      }
-    }
-
-    // The query has landed before any tile copy is issued (the compiler's own
-    // wait for these loads would otherwise sit inside the tile loop and drain
-    // the copy pipeline on every tile): vmcnt(0), expcnt/lgkmcnt unconstrained.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-
     // Copy KV tile `tile` into LDS buffer `bufi`: exactly LOADS copy
     // instructions per wave (vmcnt counts them).
     // Block id of the cache block holding this wave's keys of `tile`.
@@ -583,6 +545,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
+    // Tiles tile_a and tile_a + 1 of the first pass go out before the query.
+#pragma unroll
+    for (int k = 0; k < NB - 2; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
+
+    // Query fragments: k-step s holds channels 16 s + 8 hi .. + 8 of the row.
+    // The wave's 32 rows are consecutive in `query`; one wave-uniform buffer
+    // descriptor starts at its first row and each lane's row and chunk go in
+    // the per-lane offset (chunks past hs take an out-of-range offset and read
+    // zeros).
+    MlaState<HSP, VHSP> st;
+    const int64_t wrow0 = (int64_t)cum_b * p.H + t.row0 + 32 * w;   // first query row of the wave
+    {
+      const u32x4_t qrs = rsrc_words_u(p.query + wrow0 * p.hs, (uint32_t)(32 * p.hs * 2));
+      const int ln = opaque_lane();
+      const int lr = (32 * w + (ln & 31)) < t.nrows ? (ln & 31) : 0;
+      const uint32_t qbase = (uint32_t)(lr * p.hs * 2);
+      const int h8 = (ln >> 5) * 8;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int c0 = 16 * s + h8;
+        st.qf[s] = buffer_load_b128(qrs, c0 < p.hs ? qbase + (uint32_t)(c0 * 2) : kOutOfRange);
+      }
+      // Rotary chunks come from the RoPE'd copy the schedule launch wrote
+      // (qrot, rd channels per row); the test on the k-step is uniform and the
+      // geometry is opaque so nothing is hoisted out of the piece loop.
+      if (p.do_rotary) {
+        int ro = p.ro, rd = p.rd;
+        asm volatile("" : "+s"(ro), "+s"(rd));
+        const u32x4_t rrs = rsrc_words_u(p.qrot + wrow0 * rd, (uint32_t)(32 * rd * 2));
+        const uint32_t rbase = (uint32_t)(lr * rd * 2);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          if (16 * s + 16 > ro && 16 * s < ro + rd) {
+            const int c0 = 16 * s + h8;
+            if (c0 >= ro && c0 < ro + rd) st.qf[s] = buffer_load_b128(rrs, rbase + (uint32_t)((c0 - ro) * 2));
+          }
+        }
+      }
+    }
+
+    // The first two KV tiles of the piece are already in flight (issued
+    // before the query loads so that the two latencies overlap); the query
+    // and they have landed before the tile loop starts (the compiler's own
+    // wait for the query loads would otherwise sit inside the tile loop and
+    // drain the copy pipeline on every tile): vmcnt(0), expcnt/lgkmcnt
+    // unconstrained.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
     // LDS fragment addresses of this lane relative to a tile buffer.
     // K (QK A operand): row l32, chunk 2 s + hi; four bases cover s & 3.
     uint32_t kaddr[4], vaddr[4];
@@ -623,9 +633,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // every wave consumed before this iteration's barrier.
       constexpr int AHEAD = NB - 2;   // tiles in flight beyond the current one
       // Every iteration issues the copies of one tile (empty past the piece),
-      // so the copy wait below is the same on every tile.
+      // so the copy wait below is the same on every tile. The first pass's
+      // first AHEAD tiles were issued before the query loads.
+      if (pass > 0) {
 #pragma unroll
-      for (int k = 0; k < AHEAD; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
+        for (int k = 0; k < AHEAD; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
+      }
       {
         const u32x4_t z = {0u, 0u, 0u, 0u};
         asm volatile("s_nop 4");   // VALU write of z precedes its use as SrcA/B
@@ -745,7 +758,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         ds_write_b128_acc<(32 * cl + 8 * j) * 4>(wb[r], part);
       });
       lds_barrier();     // staged round visible (the asm writes are waited for by lgkmcnt(0))
-      for (int idx = (int)threadIdx.x; idx < RW * C8; idx += NW * 64) {
+      if (PA_MLA_EPI_FAST && t.nrows == RW && p.vhs == VHSP) {
+        // Every row and channel present: thread (r0, c8) handles staged column
+        // group c8 of rows r0, r0 + RSTEP, ...; the staging reads of a batch
+        // of NBT rows are issued before its stores.
+        constexpr int RSTEP = NW * 64 / C8;
+        constexpr int NIT = RW / RSTEP;
+        constexpr int NBT = 8;
+        static_assert(NIT % NBT == 0, "whole batches");
+        const int c8 = (int)threadIdx.x % C8, r0 = (int)threadIdx.x / C8;
+        const int sc = c8 * 8;
+        const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);
+#pragma unroll
+        for (int k0 = 0; k0 < NIT; k0 += NBT) {
+          f32x4_t v0[NBT], v1[NBT];
+#pragma unroll
+          for (int k = 0; k < NBT; ++k) {
+            v0[k] = *(const f32x4_t*)(ost + (r0 + RSTEP * (k0 + k)) * ORS + sc);
+            v1[k] = *(const f32x4_t*)(ost + (r0 + RSTEP * (k0 + k)) * ORS + sc + 4);
+          }
+          if (whole) {
+#pragma unroll
+            for (int k = 0; k < NBT; ++k) {
+              const float lr = rowl[r0 + RSTEP * (k0 + k)];
+              const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+              const float x[8] = {v0[k][0] * inv, v0[k][1] * inv, v0[k][2] * inv, v0[k][3] * inv,
+                                  v1[k][0] * inv, v1[k][1] * inv, v1[k][2] * inv, v1[k][3] * inv};
+              *(u32x4_t*)(p.out + (orow0 + r0 + RSTEP * (k0 + k)) * VHSP + cg) = pack8<DT>(x);
+            }
+          } else {
+            float* const dst0 = p.part_acc + slot * p.part_slot + (int64_t)(r0 + RSTEP * k0) * p.part_row + cg;
+#pragma unroll
+            for (int k = 0; k < NBT; ++k) {
+              float* const dst = dst0 + (int64_t)(RSTEP * k) * p.part_row;
+              *(f32x4_t*)dst = v0[k];
+              *(f32x4_t*)(dst + 4) = v1[k];
+            }
+          }
+        }
+      } else for (int idx = (int)threadIdx.x; idx < RW * C8; idx += NW * 64) {
         const int r = idx / C8;
         const int sc = (idx - r * C8) * 8;                 // staged column
         const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);   // value channel
