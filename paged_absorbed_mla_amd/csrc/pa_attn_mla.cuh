@@ -270,7 +270,7 @@ static_assert(PvSched::wait(0) >= 0 && PvSched::wait(16) >= 0 && PvSched::wait(3
 // place). full_tile (uniform): every key of the tile is visible to every
 // valid row of the wave, so no per-lane mask is formed.
 struct MlaSm {
-  f32x16_t s;        // scores of the tile, log2 units after step 0
+  f32x16_t s;        // scores of the tile (raw when the scale is fused, else log2 units after step 0)
   float tmax, m_use, psum;
   u32x4_t pf[2];     // probabilities as PV B fragments (k-steps 0 and 1), packed as they are formed
 };
@@ -280,42 +280,46 @@ template <typename DT, int HSP, int VHSP, int C>
 __device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm, int key0, int pos, int lo_row,
                                              bool full_tile, bool softcap_on, const AttnParams& p) {
   const int hi = (threadIdx.x & 63) >> 5;
+  // Scale fused into the exponent (no softcap, scale > 0): the maximum of the
+  // raw scores times the scale is the maximum logit (rounding is monotone),
+  // and each probability is 2^fma(s, scale, -reference). Otherwise step 0
+  // forms the logits and the multiplier is 1.
+  const bool fused = !softcap_on && p.scale_log2 > 0.0f;
   if constexpr (C == 0) {
-    // scale (and softcap) into log2 units
     sm.tmax = -INFINITY;
     sm.psum = 0.0f;
-    if (softcap_on) {
+    if (!fused) {
+      if (softcap_on) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sm.s[e] = softcap_log2(sm.s[e], p.scale, p.softcap, p.softcap_inv);
-    } else {
-      const float c = p.scale_log2;
+        for (int e = 0; e < 16; ++e) sm.s[e] = softcap_log2(sm.s[e], p.scale, p.softcap, p.softcap_inv);
+      } else {
+        const float c = p.scale_log2;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sm.s[e] *= c;
+        for (int e = 0; e < 16; ++e) sm.s[e] *= c;
+      }
     }
   } else if constexpr (C == 1) {
-    // mask and tile max
-    if (full_tile) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sm.tmax = fmaxf(sm.tmax, sm.s[e]);
-    } else {
+    // mask (in place, only for a tile some row does not see whole) and tile max
+    if (!full_tile) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = key0 + hi * 4 + (e & 3) + 8 * (e >> 2);
-        const float v = (j <= pos && j >= lo_row) ? sm.s[e] : -INFINITY;
-        sm.s[e] = v;
-        sm.tmax = fmaxf(sm.tmax, v);
+        sm.s[e] = (j <= pos && j >= lo_row) ? sm.s[e] : -INFINITY;
       }
     }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sm.tmax = fmaxf(sm.tmax, sm.s[e]);
   } else if constexpr (C == 2) {
-    const float tmax = max_xor32(sm.tmax);
+    const float tmax = fused ? max_xor32(sm.tmax) * p.scale_log2 : max_xor32(sm.tmax);
     st.m_seen = fmaxf(st.m_seen, tmax);
     if (st.m_ref == -INFINITY) st.m_ref = tmax;
     st.ovf |= tmax > st.m_ref + PRange<DT>::value;
     sm.m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
   } else if constexpr (C >= 3 && C < 11) {
     constexpr int k = C - 3;   // probabilities of elements 2k, 2k + 1 -> word k of the fragments
-    const float p0 = fast_exp2(sm.s[2 * k] - sm.m_use);
-    const float p1 = fast_exp2(sm.s[2 * k + 1] - sm.m_use);
+    const float mul = fused ? p.scale_log2 : 1.0f;
+    const float p0 = fast_exp2(__builtin_fmaf(sm.s[2 * k], mul, -sm.m_use));
+    const float p1 = fast_exp2(__builtin_fmaf(sm.s[2 * k + 1], mul, -sm.m_use));
     sm.psum += p0 + p1;
     sm.pf[k >> 2][k & 3] = DT::from_f32(p0) | (DT::from_f32(p1) << 16);
   } else if constexpr (C == 11) {
