@@ -141,6 +141,18 @@ __device__ __forceinline__ u32x4_t lgkm_wait_v(u32x4_t v) {
   return v;
 }
 
+// s_waitcnt lgkmcnt(N) (vmcnt and expcnt unconstrained) that no instruction
+// is scheduled across. Used where the reads it waits for and their consumers
+// are all inline assembly or fixed in program order, so unlike lgkm_wait_v it
+// does not pretend to write the read destinations (which would make the
+// compiler add a hazard wait state before the MFMA that consumes them).
+template <int N>
+__device__ __forceinline__ void lgkm_wait_fence() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // rsrc_words for a wave-uniform base: the words are forced into SGPRs.
 __device__ __forceinline__ u32x4_t rsrc_words_u(const void* base, uint32_t bytes) {
   u32x4_t r = rsrc_words(base, bytes);
@@ -216,7 +228,7 @@ __device__ __forceinline__ f32x16_t mla_qk(const u32x4_t* qf, uint32_t L, const 
     if constexpr (s % 2 == 0) {
       // Reads issued so far: k-steps 0 .. min(s + QPF - 1, NKS - 1).
       constexpr int last = (s + QPF - 1) < (NKS - 1) ? (s + QPF - 1) : (NKS - 1);
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(ka[s % QPF]), "+v"(ka[(s + 1) % QPF]) : "n"(last - (s + 1)));
+      lgkm_wait_fence<last - (s + 1)>();
     }
     sacc = DT::mfma32(ka[s % QPF], qf[s], sacc);
     if constexpr (s + QPF < NKS) ka[s % QPF] = ds_read_b128_asm<((s + QPF) >> 2) * 128>(L + kaddr[(s + QPF) & 3]);
@@ -386,8 +398,7 @@ __device__ __forceinline__ void mla_pv(MlaState<HSP, VHSP>& st, uint32_t Lv, con
     u32x4_t& b = ks == 0 ? p0[r] : p1[r];
     // Wait where a fragment is first used: V^T(ks, c) at r == 0, P(ks, r)
     // at c == 0 (later uses find it complete).
-    if constexpr (r == 0 || c == 0)
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vf[c]), "+v"(b) : "n"(PvSched::wait(n)));
+    if constexpr (r == 0 || c == 0) lgkm_wait_fence<PvSched::wait(n)>();
     PvMfma<DT>::run(st.o[4 * c + r], vf[c], b);
     // Reads issued after this MFMA (PvSched::at).
     if constexpr (n == 0) v_frag(I0{}, std::integral_constant<int, 2>{});
@@ -446,20 +457,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Copy slot sl = it * 64 + lane of this wave is LDS row 8 w + sl / CPR,
   // position sl % CPR, which holds chunk (sl % CPR) ^ swizzle(row). Its source
-  // is byte off(it) of the wave's KW cache rows; two 16-bit offsets per
-  // register. Chunks at channels >= hs get 0xFFFF, past the descriptor's range.
-  constexpr int NOFF = (LOADS + 1) / 2;
-  uint32_t load_off2[NOFF];
-#pragma unroll
-  for (int k2 = 0; k2 < NOFF; ++k2) load_off2[k2] = 0xFFFFFFFFu;
+  // is byte load_off[it] of the wave's KW cache rows (one register per copy
+  // instruction, so a copy needs no offset arithmetic). Chunks at channels
+  // >= hs get 0xFFFF, past the descriptor's range.
+  uint32_t load_off[LOADS];
 #pragma unroll
   for (int it = 0; it < LOADS; ++it) {
     const int sl = it * 64 + lane;
     const int k = sl / CPR;
     const int lc = (sl - k * CPR) ^ mla_swizzle(w * KW + k);
-    const uint32_t off = lc * 8 < p.hs ? (uint32_t)((k * p.hs + lc * 8) * 2) : 0xFFFFu;
-    const int sh = (it & 1) * 16;
-    load_off2[it >> 1] = (load_off2[it >> 1] & ~(0xFFFFu << sh)) | (off << sh);
+    load_off[it] = lc * 8 < p.hs ? (uint32_t)((k * p.hs + lc * 8) * 2) : 0xFFFFu;
   }
 
   while (u < u_end) {
@@ -529,9 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the wave's slice). Exactly LOADS of them per tile and wave (vmcnt counts
     // them). LOWER: keys below kv_lo take an out-of-range offset.
     auto copy_one = [&](const CopyPlan& c, int it, auto LOWER) {
-      uint32_t o2 = load_off2[it >> 1];
-      asm volatile("" : "+v"(o2));
-      uint32_t off = (it & 1) ? (o2 >> 16) : (o2 & 0xFFFFu);
+      uint32_t off = load_off[it];
       if constexpr (decltype(LOWER)::value) {
         const int j = c.kw0 + (it * 64 + opaque_lane()) / CPR;
         off = j >= t.kv_lo ? off : kOutOfRange;
