@@ -492,15 +492,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int lo_row = p.window >= 0 ? max(0, pos - p.window) : 0;
     const int64_t qrow = (int64_t)(cum_b + tq) * p.H + h;
     // Wave-uniform visibility bounds over the wave's valid rows: a tile with
-    // lo_max <= first key and last key <= pos_min needs no masking.
-    int pos_min = row_ok ? pos : INT_MAX, lo_max = row_ok ? lo_row : INT_MIN;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      pos_min = min(pos_min, __shfl_xor(pos_min, d));
-      lo_max = max(lo_max, __shfl_xor(lo_max, d));
+    // lo_max <= first key and last key <= pos_min needs no masking. The valid
+    // rows are consecutive and both pos and lo_row grow with the row, so the
+    // bounds are those of the wave's first and last valid row (scalar work;
+    // a cross-lane reduction here costs permute addresses that the compiler
+    // keeps in spill slots).
+    int pos_min = INT_MAX, lo_max = INT_MIN;
+    {
+      const int nval = min(32, t.nrows - 32 * w);
+      if (nval > 0) {
+        const int r0 = t.row0 + 32 * w;
+        pos_min = past_b + r0 / p.H;
+        const int pos1 = past_b + (r0 + nval - 1) / p.H;
+        lo_max = p.window >= 0 ? max(0, pos1 - p.window) : 0;
+      }
+      pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+      lo_max = __builtin_amdgcn_readfirstlane(lo_max);
     }
-    pos_min = __builtin_amdgcn_readfirstlane(pos_min);
-    lo_max = __builtin_amdgcn_readfirstlane(lo_max);
     auto tile_full = [&](int key0) { return key0 >= lo_max && key0 + KT - 1 <= pos_min; };
 
     // Copy KV tile `tile` into LDS buffer `bufi`: exactly LOADS copy
@@ -566,15 +574,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     MlaState<HSP, VHSP> st;
     const int64_t wrow0 = (int64_t)cum_b * p.H + t.row0 + 32 * w;   // first query row of the wave
     {
-      const u32x4_t qrs = rsrc_words_u(p.query + wrow0 * p.hs, (uint32_t)(32 * p.hs * 2));
+      // hs pinned to a scalar register: a value the compiler rematerialises
+      // from a spill slot here would need a vmcnt wait, and since it does not
+      // see the tile copies above that wait would drain them before the query
+      // loads go out.
+      int qhs = p.hs;
+      asm volatile("" : "+s"(qhs));
+      const u32x4_t qrs = rsrc_words_u(p.query + wrow0 * qhs, (uint32_t)(32 * qhs * 2));
       const int ln = opaque_lane();
       const int lr = (32 * w + (ln & 31)) < t.nrows ? (ln & 31) : 0;
-      const uint32_t qbase = (uint32_t)(lr * p.hs * 2);
+      const uint32_t qbase = (uint32_t)(lr * qhs * 2);
       const int h8 = (ln >> 5) * 8;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         const int c0 = 16 * s + h8;
-        st.qf[s] = buffer_load_b128(qrs, c0 < p.hs ? qbase + (uint32_t)(c0 * 2) : kOutOfRange);
+        st.qf[s] = buffer_load_b128(qrs, c0 < qhs ? qbase + (uint32_t)(c0 * 2) : kOutOfRange);
       }
       // Rotary chunks come from the RoPE'd copy the schedule launch wrote
       // (qrot, rd channels per row); the test on the k-step is uniform and the

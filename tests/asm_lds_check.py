@@ -90,6 +90,29 @@ def mfma_hazards(asm_lines, need=4):
     return found
 
 
+def loads_before_first_vm_wait(asm_lines):
+    """Register-destination buffer loads issued after the first inline-assembly
+    LDS copy (buffer_load ... lds) and before the first s_waitcnt that counts
+    vector memory operations. The compiler does not see the copies, so a
+    vmcnt wait it places for one of its own loads (a spill reload, say) also
+    drains every copy in flight; the kernel's query loads must all go out
+    before any such wait for their latency to overlap that of the first KV
+    tiles. Returns (number of such loads, line number of the wait or None)."""
+    started, n = False, 0
+    for i, ln in enumerate(asm_lines):
+        t = ln.split(";")[0].strip()
+        if not t.startswith(("buffer_load", "s_waitcnt")):
+            continue
+        if t.startswith("buffer_load"):
+            if t.endswith(" lds"):
+                started = True
+            elif started:
+                n += 1
+        elif started and "vmcnt" in t:
+            return n, i + 1
+    return n, None
+
+
 def kernel_lines(asm_text, symbol_prefix):
     """Lines of the first function whose symbol starts with symbol_prefix."""
     out, inside = [], False

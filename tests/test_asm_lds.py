@@ -10,7 +10,7 @@ import tempfile
 
 import pytest
 
-from asm_lds_check import check, kernel_lines, mfma_hazards
+from asm_lds_check import check, kernel_lines, loads_before_first_vm_wait, mfma_hazards
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -40,6 +40,10 @@ def test_mla_kernel_lds_reads_are_waited_for(inst):
     assert not found, "\n".join(f"line {a}: {b} uses {c} of the LDS read at line {d}" for a, b, c, d in found[:10])
     hz = mfma_hazards(lines)
     assert not hz, "\n".join(f"line {a}: {b} right after {c}" for a, b, c in hz[:10])
+    # 576 channels = 36 k-steps of query loads, all issued while the first two
+    # KV tiles are in flight.
+    n, at = loads_before_first_vm_wait(lines)
+    assert n >= 36, f"only {n} query loads before the vmcnt wait at line {at}"
 
 
 def test_checker_flags_a_valu_write_right_before_an_asm_mfma():
@@ -54,3 +58,11 @@ def test_checker_flags_a_copy_before_the_wait():
              "v_mov_b32 v10, v6", "s_waitcnt lgkmcnt(0)", "v_mov_b32 v11, v7"]
     found = check(lines)
     assert [f[0] for f in found] == [4]
+
+
+def test_checker_counts_loads_before_a_vm_wait():
+    lines = ["buffer_load_dwordx4 v1, s[0:3], 0 offen lds", "scratch_load_dword v0, off, off",
+             "s_waitcnt vmcnt(0)", "buffer_load_dwordx4 v[4:7], v2, s[4:7], 0 offen"]
+    assert loads_before_first_vm_wait(lines) == (0, 3)
+    lines = [lines[0], lines[3], lines[1], lines[2]]
+    assert loads_before_first_vm_wait(lines) == (1, 4)
