@@ -123,8 +123,9 @@ pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* di
 /*
  * Bytes of device workspace pa_latent_attention needs for these attrs/dims on
  * `device` (a HIP device ordinal). The workspace holds the on-device work
- * schedule and the split-KV partial results (running max, denominator and
- * unnormalised accumulator per row, float32). The result depends only on the
+ * schedule and the split-KV partial results (float32 running max and
+ * denominator per row, and the piece's normalised output row in the output
+ * type). The result depends only on the
  * arguments and the device's compute-unit count; it is written to *bytes.
  */
 pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims,

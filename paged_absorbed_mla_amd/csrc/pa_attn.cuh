@@ -37,9 +37,9 @@
 //     masked probability (0) never meets a non-finite cache value.
 //   * Work split (flash-decoding): an on-device scheduler lays the KV tiles of
 //     all query tiles end to end and gives every workgroup an equal share.
-//     A query tile whose tiles span several workgroups gets one float32 partial
-//     (max, denominator, unnormalised accumulator) per piece, merged by the
-//     combine kernel with a log-sum-exp weighting.
+//     A query tile whose tiles span several workgroups gets one partial per
+//     piece (float32 max and denominator, normalised output in the output
+//     type), merged by the combine kernel with a log-sum-exp weighting.
 #pragma once
 
 #include <type_traits>
@@ -75,9 +75,9 @@ struct AttnParams {
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
   const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
-  float* part_acc;          // partial accumulators: slot s, row r at s * part_slot + r * part_row
-  int64_t part_slot;        // floats between slots (padded: not a power of two)
-  int part_row;             // floats between rows (VHSP + 4)
+  uint16_t* part_o;         // partial outputs acc / l in the output type: slot s, row r at s * part_slot + r * part_row
+  int64_t part_slot;        // elements between slots (padded: not a power of two)
+  int part_row;             // elements between rows (VHSP + 8)
   const uint16_t* qrot;     // [T * H][rd]: query rotary channels after RoPE (four-wave 576 kernel)
   int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
@@ -591,49 +591,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     __syncthreads();
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    if (whole) {
-      if (row_ok) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        uint16_t* orow = p.out + qrow * p.vhs;
-        if (p.vhs == VHSP) {
-          // Lane writes channels mt*32 + hi*4 + 8*grp .. + 3 of its row: one base
-          // address, immediate offsets.
-          uint16_t* ob = orow + hi * 4;
+    // A whole query tile writes its output rows. A split-KV piece writes its
+    // own normalised output acc / l, rounded to the output type, into its
+    // partial slot (rows padded to VHSP channels) and (m, l) in float32; the
+    // combine merges the pieces.
+    if (row_ok) {
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      uint16_t* orow;
+      if (whole) {
+        orow = p.out + qrow * p.vhs;
+      } else {
+        const int64_t slot = (int64_t)t.part_base + (wr - t.w_first);
+        if (hi == 0) {
+          float* ml = p.part_ml + (slot * RW + rloc) * 2;
+          ml[0] = st.m_run;
+          ml[1] = l_tot;
+        }
+        orow = p.part_o + slot * p.part_slot + (int64_t)rloc * p.part_row;
+      }
+      if (!whole || p.vhs == VHSP) {
+        // Lane writes channels mt*32 + hi*4 + 8*grp .. + 3 of its row: one base
+        // address, immediate offsets.
+        uint16_t* ob = orow + hi * 4;
 #pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-              const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
-              const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
-              const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
-              const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
-              *(u32x2_t*)(ob + mt * 32 + 8 * grp) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-            }
-          }
-        } else {
-          for (int mt = 0; mt < NMT; ++mt) {
-            for (int e = 0; e < 16; ++e) {
-              const int c = mt * 32 + hi * 4 + 8 * (e >> 2) + (e & 3);
-              if (c < p.vhs) orow[c] = (uint16_t)DT::from_f32(st.o[mt][e] * inv);
-            }
+          for (int grp = 0; grp < 4; ++grp) {
+            const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
+            const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
+            const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
+            const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
+            *(u32x2_t*)(ob + mt * 32 + 8 * grp) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
           }
         }
-      }
-    } else {
-      const int64_t slot = (int64_t)t.part_base + (wr - t.w_first);
-      if (hi == 0) {
-        float* ml = p.part_ml + (slot * RW + rloc) * 2;
-        ml[0] = st.m_run;
-        ml[1] = l_tot;
-      }
-      float* acc = p.part_acc + slot * p.part_slot + (int64_t)rloc * p.part_row;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int c0 = mt * 32 + hi * 4 + 8 * grp;
-          *(f32x4_t*)(acc + c0) =
-              f32x4_t{st.o[mt][4 * grp], st.o[mt][4 * grp + 1], st.o[mt][4 * grp + 2], st.o[mt][4 * grp + 3]};
+      } else {
+        for (int mt = 0; mt < NMT; ++mt) {
+          for (int e = 0; e < 16; ++e) {
+            const int c = mt * 32 + hi * 4 + 8 * (e >> 2) + (e & 3);
+            if (c < p.vhs) orow[c] = (uint16_t)DT::from_f32(st.o[mt][e] * inv);
+          }
         }
       }
     }
@@ -643,27 +639,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Merge the partials of every query tile that several workgroups processed:
-// with M = max_i m_i (log2 domain) and w_i = 2^(m_i - M),
-// out = sum_i w_i acc_i / sum_i w_i l_i, rounded to nearest even.
+// Merge the partials of every query tile that several workgroups processed.
+// Piece i of a row holds its normalised output o_i = acc_i / l_i (output
+// type), its running max m_i (log2 domain) and denominator l_i; with
+// M = max_i m_i and c_i = 2^(m_i - M) l_i, out = sum_i c_i o_i / sum_i c_i
+// (float32), rounded to nearest even.
 // Grid: (query tiles, RW / kCombineRows) of 256 threads. TPR threads share a
-// row; thread j of a row owns the 4-channel groups j, j + TPR, j + 2 TPR, ...
-// (so each load instruction covers contiguous bytes of a row). Every thread forms its row's
-// weights itself from the (m, l) pairs. Up to QA pieces: the pairs and all
-// slice loads go out together (one round trip). More pieces: the pairs are
-// read 8 pieces at a time, then the slices 4 pieces at a time with all their
-// 16-byte loads in flight together (coalesced across the row's threads).
+// row; thread j of a row owns the 8-channel groups j, j + TPR, j + 2 TPR, ...
+// (so each load instruction covers contiguous bytes of a row). Every thread
+// forms its row's weights itself from the (m, l) pairs. Up to QA pieces: the
+// pairs and all slice loads go out together (one round trip). More pieces:
+// the pairs are read 8 pieces at a time, then the slices 4 pieces at a time
+// with all their 16-byte loads in flight together.
 constexpr int kCombineRows = 16;
 
 template <typename DT, int VHSP, int RW>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  constexpr int TPR = (VHSP / 4) < 16 ? (VHSP / 4) : 16;   // threads per row
-  constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 4)
+  constexpr int TPR = (VHSP / 8) < 16 ? (VHSP / 8) : 16;   // threads per row
+  constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 8)
   constexpr int ROWS = 256 / TPR;                          // rows per pass
-  constexpr int NV = CPT / 4;
+  constexpr int NV = CPT / 8;
   constexpr int QM = 8;                                    // pieces per batch of (m, l) loads
-  constexpr int QA = 4;                                    // pieces per batch of accumulator loads
-  static_assert(CPT % 4 == 0 && CPT * TPR == VHSP, "channel split");
+  constexpr int QA = 4;                                    // pieces per batch of slice loads
+  static_assert(CPT % 8 == 0 && CPT * TPR == VHSP, "channel split");
   const int i = blockIdx.x;
   if (i >= ld_uniform(p.header + 1)) return;
   const MTile t = ld_uniform_tile(p.mt + i);
@@ -672,18 +670,33 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   if (r0 >= t.nrows) return;
   const int nq = t.npieces;
   const int cum_b = ld_uniform(p.cumseq + t.b);
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
     const int r = r0 + rr;
     if (r >= t.nrows) continue;
-    const int c0 = (threadIdx.x % TPR) * 4;                 // channel of group 0; group v at c0 + 4 TPR v
+    const int c0 = (threadIdx.x % TPR) * 8;                 // channel of group 0; group v at c0 + 8 TPR v
     if (c0 >= p.vhs) continue;
     const float* ml = p.part_ml + ((int64_t)t.part_base * RW + r) * 2;   // piece q at + q * RW * 2
-    const float* pa0 = p.part_acc + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;   // piece q at + q * part_slot
-    f32x4_t acc[NV];
+    // Piece q's slice at + q * part_slot (16-byte aligned: row and slot strides are multiples of 8 elements).
+    const uint16_t* po0 = p.part_o + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;
+    float acc[NV][8];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
+    auto add = [&](float wgt, const u32x4_t (&a)[NV]) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float x[8];
+        unpack8<DT>(a[v], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] += wgt * x[e];
+      }
+    };
     if (nq <= QA) {
       // Up to QA pieces (the usual case): the (m, l) pairs and every slice
       // load are issued together, one memory round trip per row.
-      f32x4_t a[QA][NV];
+      u32x4_t a[QA][NV];
       float m[QA], l[QA];
 #pragma unroll
       for (int k = 0; k < QA; ++k) {
@@ -691,83 +704,71 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
         const int q = ok ? k : 0;
         m[k] = ok ? ml[(int64_t)q * RW * 2] : -INFINITY;
         l[k] = ok ? ml[(int64_t)q * RW * 2 + 1] : 0.0f;
-        const f32x4_t* src = (const f32x4_t*)(pa0 + (int64_t)q * p.part_slot);
+        const u32x4_t* src = (const u32x4_t*)(po0 + (int64_t)q * p.part_slot);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) a[k][v] = ok ? src[v * TPR] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < NV; ++v) a[k][v] = ok ? src[v * TPR] : zero4;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int k = 0; k < QA; ++k) mx = fmaxf(mx, m[k]);
-      float wq[QA], den = 0.0f;
+      float cq[QA], den = 0.0f;
 #pragma unroll
       for (int k = 0; k < QA; ++k) {
-        wq[k] = m[k] == -INFINITY ? 0.0f : fast_exp2(m[k] - mx);
-        den += wq[k] * l[k];
+        cq[k] = m[k] == -INFINITY ? 0.0f : fast_exp2(m[k] - mx) * l[k];
+        den += cq[k];
       }
       const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < QA; ++k)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) acc[v] += (wq[k] * inv) * a[k][v];
+      for (int k = 0; k < QA; ++k) add(cq[k] * inv, a[k]);
     } else {
-    // Reference max and denominator: one batch of (m, l) loads per QM pieces.
-    float mx = -INFINITY, den = 0.0f;
-    for (int q0 = 0; q0 < nq; q0 += QM) {
-      float m[QM], l[QM];
+      // Reference max and denominator: one batch of (m, l) loads per QM pieces.
+      float mx = -INFINITY, den = 0.0f;
+      for (int q0 = 0; q0 < nq; q0 += QM) {
+        float m[QM], l[QM];
 #pragma unroll
-      for (int k = 0; k < QM; ++k) {
-        const bool ok = q0 + k < nq;
-        m[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2] : -INFINITY;
-        l[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2 + 1] : 0.0f;
+        for (int k = 0; k < QM; ++k) {
+          const bool ok = q0 + k < nq;
+          m[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2] : -INFINITY;
+          l[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2 + 1] : 0.0f;
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < QM; ++k) bm = fmaxf(bm, m[k]);
+        const float nm = fmaxf(mx, bm);
+        den = (mx == -INFINITY) ? 0.0f : den * fast_exp2(mx - nm);
+#pragma unroll
+        for (int k = 0; k < QM; ++k) den += (m[k] == -INFINITY) ? 0.0f : fast_exp2(m[k] - nm) * l[k];
+        mx = nm;
       }
-      float bm = -INFINITY;
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      // Weighted sum of the row slices.
+      for (int q0 = 0; q0 < nq; q0 += QA) {
+        u32x4_t a[QA][NV];
+        float wq[QA];
 #pragma unroll
-      for (int k = 0; k < QM; ++k) bm = fmaxf(bm, m[k]);
-      const float nm = fmaxf(mx, bm);
-      den = (mx == -INFINITY) ? 0.0f : den * fast_exp2(mx - nm);
+        for (int k = 0; k < QA; ++k) {
+          const bool ok = q0 + k < nq;
+          const int q = ok ? q0 + k : q0;
+          const u32x4_t* src = (const u32x4_t*)(po0 + (int64_t)q * p.part_slot);
 #pragma unroll
-      for (int k = 0; k < QM; ++k) den += (m[k] == -INFINITY) ? 0.0f : fast_exp2(m[k] - nm) * l[k];
-      mx = nm;
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    // Weighted sum of the row slices.
+          for (int v = 0; v < NV; ++v) a[k][v] = src[v * TPR];
+          const float m = ml[(int64_t)q * RW * 2], l = ml[(int64_t)q * RW * 2 + 1];
+          wq[k] = (!ok || m == -INFINITY) ? 0.0f : fast_exp2(m - mx) * l * inv;
+        }
 #pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int q0 = 0; q0 < nq; q0 += QA) {
-      f32x4_t a[QA][NV];
-      float wq[QA];
-#pragma unroll
-      for (int k = 0; k < QA; ++k) {
-        const bool ok = q0 + k < nq;
-        const int q = ok ? q0 + k : q0;
-        const f32x4_t* src = (const f32x4_t*)(pa0 + (int64_t)q * p.part_slot);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) a[k][v] = src[v * TPR];
-        const float m = ml[(int64_t)q * RW * 2];
-        wq[k] = (!ok || m == -INFINITY) ? 0.0f : fast_exp2(m - mx) * inv;
+        for (int k = 0; k < QA; ++k) add(wq[k], a[k]);
       }
-#pragma unroll
-      for (int k = 0; k < QA; ++k)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) acc[v] += wq[k] * a[k][v];
-    }
     }
     uint16_t* orow = p.out + ((int64_t)cum_b * p.H + t.row0 + r) * p.vhs + c0;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int c = c0 + 4 * TPR * v;
-      if ((p.vhs & 3) == 0) {
-        if (c < p.vhs) {
-          const uint32_t e0 = DT::from_f32(acc[v][0]), e1 = DT::from_f32(acc[v][1]);
-          const uint32_t e2 = DT::from_f32(acc[v][2]), e3 = DT::from_f32(acc[v][3]);
-          *(u32x2_t*)(orow + 4 * TPR * v) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-        }
+      const int c = c0 + 8 * TPR * v;
+      if ((p.vhs & 7) == 0) {
+        if (c < p.vhs) *(u32x4_t*)(orow + 8 * TPR * v) = pack8<DT>(acc[v]);
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (c + k < p.vhs) orow[4 * TPR * v + k] = (uint16_t)DT::from_f32(acc[v][k]);
+        for (int k = 0; k < 8; ++k)
+          if (c + k < p.vhs) orow[8 * TPR * v + k] = (uint16_t)DT::from_f32(acc[v][k]);
       }
     }
   }

@@ -385,11 +385,11 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_sched = off; off = align256(off + (size_t)L.sched_ints * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
-  // Partial accumulators: rows padded by 16 bytes and slots by 256 bytes so
-  // concurrent pieces do not sit at power-of-two strides.
-  L.part_row = cfg.vhsp + 4;
+  // Partial outputs (16-bit, the output type): rows padded by 16 bytes and
+  // slots by 128 bytes so concurrent pieces do not sit at power-of-two strides.
+  L.part_row = cfg.vhsp + 8;
   L.part_slot = (int64_t)RW * L.part_row + 64;
-  L.off_part_acc = off; off = align256(off + (size_t)L.part_cap * L.part_slot * sizeof(float));
+  L.off_part_o = off; off = align256(off + (size_t)L.part_cap * L.part_slot * sizeof(uint16_t));
   L.off_qrot = 0;
   if (cfg.wide == 2 && g.do_rotary) {
     L.off_qrot = off;
@@ -458,7 +458,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.mt = sp.mt;
   ap.zero16 = (const uint16_t*)sp.zero16;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
-  ap.part_acc = (float*)(wsb + ws.off_part_acc);
+  ap.part_o = (uint16_t*)(wsb + ws.off_part_o);
   ap.part_slot = ws.part_slot;
   ap.part_row = ws.part_row;
   ap.qrot = sp.qrot;

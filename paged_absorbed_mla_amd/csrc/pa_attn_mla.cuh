@@ -40,9 +40,6 @@ namespace pa {
 #ifndef PA_MLA_QPF
 #define PA_MLA_QPF 4
 #endif
-#ifndef PA_MLA_EPI_FAST
-#define PA_MLA_EPI_FAST 0
-#endif
 #ifndef PA_MLA_VPF
 #define PA_MLA_VPF 3
 #endif
@@ -745,9 +742,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // staged as float32 rows in two rounds, round k holding channel blocks
     // 2k, 2k + 1 of every wave (wave w's 64 channels at staged column 64 w),
     // written straight from the accumulation registers; then every thread
-    // normalises (whole tile) or copies (partial result) 8 consecutive
-    // channels of a row with coalesced stores. Rows are padded by 16 bytes
-    // against bank conflicts.
+    // normalises 8 consecutive channels of a row and stores them, rounded to
+    // the output type, with coalesced stores into the output (whole tile) or
+    // the piece's partial slot (split-KV; (m, l) go beside it in float32).
+    // Rows are padded by 16 bytes against bank conflicts.
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     constexpr int QCH = VHSP / NW;                         // value channels per wave
     constexpr int RCH = QCH / 2;                           // per wave and round
@@ -770,6 +768,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int r = 0; r < NW; ++r) wb[r] = lds_addr(ost) + (uint32_t)(((32 * r + l32) * ORS + RCH * w + 4 * hi) * 4);
     const int64_t orow0 = (int64_t)cum_b * p.H + t.row0;  // output row of local row 0
+    // Read-out of a full tile (every row, every value channel): RSTEP rows per
+    // pass of the workgroup, NIT passes, reciprocals of the rows' denominators
+    // formed once for both rounds.
+    const bool full_tile = t.nrows == RW && p.vhs == VHSP;
+    constexpr int RSTEP = NW * 64 / C8;
+    constexpr int NIT = RW / RSTEP;
+    constexpr int NBT = 4;
+    static_assert(NIT % NBT == 0, "whole batches");
+    const int r0f = (int)threadIdx.x / C8;
+    // (Defined on every path: an undefined array would let the compiler carry
+    // the previous piece's values around the piece loop.)
+    float inv_r[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) inv_r[k] = 0.0f;
     static_for<0, 2>([&](auto RD) {
       constexpr int rd = decltype(RD)::value;
       static_for<0, 2 * NW * 4>([&](auto K) {
@@ -781,42 +793,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         ds_write_b128_acc<(32 * cl + 8 * j) * 4>(wb[r], part);
       });
       lds_barrier();     // staged round visible (the asm writes are waited for by lgkmcnt(0))
-      if (PA_MLA_EPI_FAST && t.nrows == RW && p.vhs == VHSP) {
+      if (full_tile) {
         // Every row and channel present: thread (r0, c8) handles staged column
-        // group c8 of rows r0, r0 + RSTEP, ...; the staging reads of a batch
-        // of NBT rows are issued before its stores.
-        constexpr int RSTEP = NW * 64 / C8;
-        constexpr int NIT = RW / RSTEP;
-        constexpr int NBT = 8;
-        static_assert(NIT % NBT == 0, "whole batches");
-        const int c8 = (int)threadIdx.x % C8, r0 = (int)threadIdx.x / C8;
+        // group c8 of rows r0, r0 + RSTEP, ...: the staging reads of a batch
+        // of NBT rows go out before its stores, with no per-item tests (with
+        // one wave per SIMD nothing else hides an LDS round trip per row).
+        const int c8 = (int)threadIdx.x % C8;
         const int sc = c8 * 8;
         const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);
+        if constexpr (rd == 0) {
+#pragma unroll
+          for (int k = 0; k < NIT; ++k) {
+            const float lr = rowl[r0f + RSTEP * k];
+            inv_r[k] = lr > 0.0f ? 1.0f / lr : 0.0f;
+          }
+        }
+        uint16_t* const dst0 = whole ? p.out + (orow0 + r0f) * VHSP + cg
+                                     : p.part_o + slot * p.part_slot + (int64_t)r0f * p.part_row + cg;
+        const int64_t dstep = whole ? (int64_t)RSTEP * VHSP : (int64_t)RSTEP * p.part_row;
+        const float* const src0 = ost + r0f * ORS + sc;
 #pragma unroll
         for (int k0 = 0; k0 < NIT; k0 += NBT) {
           f32x4_t v0[NBT], v1[NBT];
 #pragma unroll
           for (int k = 0; k < NBT; ++k) {
-            v0[k] = *(const f32x4_t*)(ost + (r0 + RSTEP * (k0 + k)) * ORS + sc);
-            v1[k] = *(const f32x4_t*)(ost + (r0 + RSTEP * (k0 + k)) * ORS + sc + 4);
+            v0[k] = *(const f32x4_t*)(src0 + (k0 + k) * RSTEP * ORS);
+            v1[k] = *(const f32x4_t*)(src0 + (k0 + k) * RSTEP * ORS + 4);
           }
-          if (whole) {
 #pragma unroll
-            for (int k = 0; k < NBT; ++k) {
-              const float lr = rowl[r0 + RSTEP * (k0 + k)];
-              const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-              const float x[8] = {v0[k][0] * inv, v0[k][1] * inv, v0[k][2] * inv, v0[k][3] * inv,
-                                  v1[k][0] * inv, v1[k][1] * inv, v1[k][2] * inv, v1[k][3] * inv};
-              *(u32x4_t*)(p.out + (orow0 + r0 + RSTEP * (k0 + k)) * VHSP + cg) = pack8<DT>(x);
-            }
-          } else {
-            float* const dst0 = p.part_acc + slot * p.part_slot + (int64_t)(r0 + RSTEP * k0) * p.part_row + cg;
-#pragma unroll
-            for (int k = 0; k < NBT; ++k) {
-              float* const dst = dst0 + (int64_t)(RSTEP * k) * p.part_row;
-              *(f32x4_t*)dst = v0[k];
-              *(f32x4_t*)(dst + 4) = v1[k];
-            }
+          for (int k = 0; k < NBT; ++k) {
+            const float inv = inv_r[k0 + k];
+            const float x[8] = {v0[k][0] * inv, v0[k][1] * inv, v0[k][2] * inv, v0[k][3] * inv,
+                                v1[k][0] * inv, v1[k][1] * inv, v1[k][2] * inv, v1[k][3] * inv};
+            *(u32x4_t*)(dst0 + (k0 + k) * dstep) = pack8<DT>(x);
           }
         }
       } else for (int idx = (int)threadIdx.x; idx < RW * C8; idx += NW * 64) {
@@ -826,21 +835,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (r >= t.nrows || cg >= p.vhs) continue;
         const f32x4_t v0 = *(const f32x4_t*)(ost + r * ORS + sc);
         const f32x4_t v1 = *(const f32x4_t*)(ost + r * ORS + sc + 4);
-        if (whole) {
-          const float lr = rowl[r];
-          const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-          const float x[8] = {v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv,
-                              v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv};
-          uint16_t* dst = p.out + (orow0 + r) * p.vhs + cg;
-          if (cg + 8 <= p.vhs && (p.vhs & 7) == 0) {
-            *(u32x4_t*)dst = pack8<DT>(x);
-          } else {
-            for (int k = 0; k < 8 && cg + k < p.vhs; ++k) dst[k] = (uint16_t)DT::from_f32(x[k]);
-          }
+        const float lr = rowl[r];
+        const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+        const float x[8] = {v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv,
+                            v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv};
+        // Output row, or the piece's partial row (padded to VHSP channels).
+        uint16_t* dst = whole ? p.out + (orow0 + r) * p.vhs + cg
+                              : p.part_o + slot * p.part_slot + (int64_t)r * p.part_row + cg;
+        if (!whole || (cg + 8 <= p.vhs && (p.vhs & 7) == 0)) {
+          *(u32x4_t*)dst = pack8<DT>(x);
         } else {
-          float* dst = p.part_acc + slot * p.part_slot + (int64_t)r * p.part_row + cg;
-          *(f32x4_t*)dst = v0;
-          *(f32x4_t*)(dst + 4) = v1;
+          for (int k = 0; k < 8 && cg + k < p.vhs; ++k) dst[k] = (uint16_t)DT::from_f32(x[k]);
         }
       }
       lds_barrier();     // staging area free again

@@ -45,11 +45,11 @@ struct WsLayout {
   int grid;             // workgroups of the attention launch
   int ranges;           // unit ranges of the schedule (one per workgroup)
   int64_t part_cap;     // partial-result slots
-  size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_zero, off_part_ml, off_part_acc;
+  size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_zero, off_part_ml, off_part_o;
   int64_t sched_ints;   // scheduler scratch (int32) when it does not fit its LDS
   size_t off_qrot;      // rotated query channels [T * H][rd] (0: none)
-  int64_t part_slot;    // floats between partial-result slots
-  int part_row;         // floats between partial-result rows
+  int64_t part_slot;    // 16-bit elements between partial-result slots
+  int part_row;         // 16-bit elements between partial-result rows
   size_t total;
 };
 
