@@ -129,6 +129,16 @@ __device__ __forceinline__ int opaque_lane() {
   return l;
 }
 
+// Lane id formed afresh from the exec-mask bit count (no memory access): the
+// opaque all-ones mask keeps the compiler from reusing an earlier lane id,
+// which after a long loop would sit in a spill slot, and from holding values
+// derived from it live across that loop.
+__device__ __forceinline__ int fresh_lane() {
+  uint32_t m = ~0u;
+  asm volatile("" : "+s"(m));
+  return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data

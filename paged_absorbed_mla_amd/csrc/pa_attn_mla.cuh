@@ -173,6 +173,14 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sum of lane l's value and lane l ^ 32's (the same swap; the two halves get
+// bit-identical sums since addition commutes). Needs no lane id, unlike a
+// permute, whose address the compiler would keep in a spill slot.
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // State one wave carries across the KV tiles of a piece.
 template <int HSP, int VHSP>
 struct MlaState {
@@ -746,7 +754,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the output type, with coalesced stores into the output (whole tile) or
     // the piece's partial slot (split-KV; (m, l) go beside it in float32).
     // Rows are padded by 16 bytes against bank conflicts.
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    const float l_tot = sum_xor32(st.l_run);
     constexpr int QCH = VHSP / NW;                         // value channels per wave
     constexpr int RCH = QCH / 2;                           // per wave and round
     constexpr int SCOL = NW * RCH;                         // staged columns per round
@@ -756,17 +764,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(RCH == 64, "two 32-channel blocks per wave and round");
     float* const ost = (float*)lds_raw;
     float* const rowl = ost + RW * ORS;                    // [RW] denominators
-    if (hi == 0) rowl[rloc] = l_tot;
+    // Lane quantities re-derived here rather than carried across the tile loop.
+    const int eln = fresh_lane();
+    const int el32 = eln & 31, ehi = eln >> 5;
+    const int erloc = w * 32 + el32;
+    const int etid = w * 64 + eln;
+    if (ehi == 0) rowl[erloc] = l_tot;
     const int64_t slot = whole ? 0 : (int64_t)t.part_base + (wr - t.w_first);
-    if (!whole && hi == 0 && row_ok) {
-      float* ml = p.part_ml + (slot * RW + rloc) * 2;
+    if (!whole && ehi == 0 && erloc < t.nrows) {
+      float* ml = p.part_ml + (slot * RW + erloc) * 2;
       ml[0] = st.m_ref;
       ml[1] = l_tot;
     }
     // Lane's staging address for row block r: row 32 r + l32, column 64 w + 4 hi.
     uint32_t wb[NW];
 #pragma unroll
-    for (int r = 0; r < NW; ++r) wb[r] = lds_addr(ost) + (uint32_t)(((32 * r + l32) * ORS + RCH * w + 4 * hi) * 4);
+    for (int r = 0; r < NW; ++r) wb[r] = lds_addr(ost) + (uint32_t)(((32 * r + el32) * ORS + RCH * w + 4 * ehi) * 4);
     const int64_t orow0 = (int64_t)cum_b * p.H + t.row0;  // output row of local row 0
     // Read-out of a full tile (every row, every value channel): RSTEP rows per
     // pass of the workgroup, NIT passes, reciprocals of the rows' denominators
@@ -776,7 +789,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int NIT = RW / RSTEP;
     constexpr int NBT = 4;
     static_assert(NIT % NBT == 0, "whole batches");
-    const int r0f = (int)threadIdx.x / C8;
+    const int r0f = etid / C8;
     // (Defined on every path: an undefined array would let the compiler carry
     // the previous piece's values around the piece loop.)
     float inv_r[NIT];
@@ -798,7 +811,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // group c8 of rows r0, r0 + RSTEP, ...: the staging reads of a batch
         // of NBT rows go out before its stores, with no per-item tests (with
         // one wave per SIMD nothing else hides an LDS round trip per row).
-        const int c8 = (int)threadIdx.x % C8;
+        const int c8 = etid % C8;
         const int sc = c8 * 8;
         const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);
         if constexpr (rd == 0) {
@@ -828,7 +841,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             *(u32x4_t*)(dst0 + (k0 + k) * dstep) = pack8<DT>(x);
           }
         }
-      } else for (int idx = (int)threadIdx.x; idx < RW * C8; idx += NW * 64) {
+      } else for (int idx = etid; idx < RW * C8; idx += NW * 64) {
         const int r = idx / C8;
         const int sc = (idx - r * C8) * 8;                 // staged column
         const int cg = (sc / RCH) * QCH + rd * RCH + (sc % RCH);   // value channel
