@@ -170,7 +170,8 @@ pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims
  * spread evenly over the device's compute units, long key ranges split and
  * merged by a log-sum-exp combine); split_kv == 0 gives every query tile to a
  * single workgroup (no partial results, no combine). The two agree up to
- * float32 rounding; tests use this to check the combine.
+ * rounding (float32 accumulation order, and each piece's output rounded to
+ * the output type before the combine); tests use this to check the combine.
  */
 pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
                                      pa_dtype dtype, const void* query, const void* key_cache,

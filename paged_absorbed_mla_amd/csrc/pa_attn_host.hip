@@ -116,7 +116,7 @@ __device__ void query_rope_chunk(const SchedParams& p, int64_t idx, const int32_
 constexpr int kSchedLdsInts = 12288;
 
 __host__ __device__ inline int64_t sched_ints(int B, int64_t max_mtiles, int grid) {
-  return 3 * (int64_t)B + 2 + 7 * max_mtiles + 1 + 2 * (int64_t)grid + 1;
+  return 3 * (int64_t)B + 2 + 9 * max_mtiles + 1 + 2 * (int64_t)grid + 1;
 }
 
 template <bool IN_LDS>
@@ -132,6 +132,8 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   int32_t* const tkv = trow + 2 * p.max_mtiles;        // [max_mtiles] kv_lo, kv_hi (2 x)
   int32_t* const wr = tkv + 2 * p.max_mtiles;          // [grid + 1] unit range of every workgroup
   int32_t* const wt = wr + (p.grid + 1);               // [grid] query tile of every workgroup
+  int32_t* const tw0 = wt + p.grid;                    // [max_mtiles] first workgroup of each tile
+  int32_t* const tw1 = tw0 + p.max_mtiles;             // [max_mtiles] last workgroup of each tile
 
   for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
     cum[b] = p.cumseq[b];
@@ -189,6 +191,12 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   // each of them writes its partial slot.
   const int64_t alpha = p.piece_units;
   const int64_t Uv = U + alpha * M;
+  // Cut x(w) = floor(w Uv / grid) as w q + floor(w r / grid) with Uv = q grid
+  // + r: one 64-bit division per thread instead of one per workgroup
+  // (w r < grid^2 fits 32 bits for grids below 65536, the split launches'
+  // compute-unit multiples).
+  const int64_t vq = Uv / p.grid;
+  const uint32_t vr = (uint32_t)(Uv - vq * p.grid);
   for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
     int32_t v;
     if (!p.split_kv) {
@@ -196,7 +204,9 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     } else if (M == 0) {
       v = 0;
     } else {
-      const int64_t x = Uv >= p.grid ? ((int64_t)w * Uv) / p.grid : min((int64_t)w, Uv);
+      const int64_t x = Uv < p.grid ? min((int64_t)w, Uv)
+                        : p.grid < 65536 ? (int64_t)w * vq + (int64_t)(((uint32_t)w * vr) / (uint32_t)p.grid)
+                                         : ((int64_t)w * Uv) / p.grid;
       int lo = 0, hi = M - 1;   // last tile whose virtual start is <= x
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -214,6 +224,8 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     const int w0 = wg_of_unit(wr, p.grid, u0[i]);
     const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
     np[i] = w1 - w0 + 1;
+    tw0[i] = w0;
+    tw1[i] = w1;
   }
   for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
     const int uw = wr[w];
@@ -241,10 +253,8 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     t.kv_lo = tkv[2 * i];
     t.kv_hi = tkv[2 * i + 1];
     t.unit0 = u0[i];
-    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
-    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
-    t.w_first = w0;
-    t.npieces = w1 - w0 + 1;
+    t.w_first = tw0[i];
+    t.npieces = tw1[i] - tw0[i] + 1;
     t.part_base = np[i];
     t.pad[0] = t.pad[1] = t.pad[2] = 0;
     p.mt[i] = t;

@@ -572,12 +572,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int k = 0; k < NB - 2; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
 
     // Query fragments: k-step s holds channels 16 s + 8 hi .. + 8 of the row.
-    // The wave's 32 rows are consecutive in `query`; one wave-uniform buffer
-    // descriptor starts at its first row and each lane's row and chunk go in
-    // the per-lane offset (chunks past hs take an out-of-range offset and read
-    // zeros).
+    // The tile's rows are consecutive in `query`; one buffer descriptor covers
+    // exactly them (from the tile's first row) and each lane's row and chunk
+    // go in the per-lane offset. Rows past the tile read the tile's row 0, so
+    // every read stays inside the tile; chunks past hs take an out-of-range
+    // offset and read zeros.
     MlaState<HSP, VHSP> st;
-    const int64_t wrow0 = (int64_t)cum_b * p.H + t.row0 + 32 * w;   // first query row of the wave
+    const int64_t trow0 = (int64_t)cum_b * p.H + t.row0;   // first query row of the tile
     {
       // hs pinned to a scalar register: a value the compiler rematerialises
       // from a spill slot here would need a vmcnt wait, and since it does not
@@ -585,9 +586,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // loads go out.
       int qhs = p.hs;
       asm volatile("" : "+s"(qhs));
-      const u32x4_t qrs = rsrc_words_u(p.query + wrow0 * qhs, (uint32_t)(32 * qhs * 2));
+      const u32x4_t qrs = rsrc_words_u(p.query + trow0 * qhs, (uint32_t)(t.nrows * qhs * 2));
       const int ln = opaque_lane();
-      const int lr = (32 * w + (ln & 31)) < t.nrows ? (ln & 31) : 0;
+      const int lr = (32 * w + (ln & 31)) < t.nrows ? 32 * w + (ln & 31) : 0;
       const uint32_t qbase = (uint32_t)(lr * qhs * 2);
       const int h8 = (ln >> 5) * 8;
 #pragma unroll
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (p.do_rotary) {
         int ro = p.ro, rd = p.rd;
         asm volatile("" : "+s"(ro), "+s"(rd));
-        const u32x4_t rrs = rsrc_words_u(p.qrot + wrow0 * rd, (uint32_t)(32 * rd * 2));
+        const u32x4_t rrs = rsrc_words_u(p.qrot + trow0 * rd, (uint32_t)(t.nrows * rd * 2));
         const uint32_t rbase = (uint32_t)(lr * rd * 2);
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
@@ -736,7 +737,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // every wave passed the barrier; the flags sit in the first buffer).
       lds_barrier();
       int* const vote = (int*)lds_raw;
-      if (lane == 0) vote[w] = __any(st.ovf) ? 1 : 0;
+      // Every lane takes part in the ballot (taken before the one-lane
+      // store); rows past the tile (duplicates of its row 0, unmasked where
+      // the wave has no valid row) do not vote.
+      const int vl = fresh_lane();
+      const bool any_ovf = __any(st.ovf && (w * 32 + (vl & 31) < t.nrows));
+      if (vl == 0) vote[w] = any_ovf ? 1 : 0;
       lds_barrier();
       const int again = vote[0] | vote[1] | vote[2] | vote[3];
       lds_barrier();     // votes read before the buffers are reused

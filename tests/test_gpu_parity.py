@@ -226,6 +226,44 @@ def test_edge_case_dsv3(name):
     _edge(_spec(name=name, **kw))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_second_pass_on_score_jump(dtype):
+    """Fixed-reference softmax, second pass: an old key whose score exceeds
+    its piece's first-tile reference by more than the probability type can
+    represent (planted key = q / 4: jump ~ |q|^2 / 4 * scale * log2(e) ~ 180
+    log2 units, against first-tile maxima near 20; cache and key values have
+    standard deviation 1/4, so outputs stay within 1 and the absolute
+    tolerance is not eaten by the output's own rounding) forces the workgroup
+    to redo the piece with exact maxima; without that pass the probability is
+    infinite. The jumps are planted for rows that are not the first of their
+    wave (heads 37 and 5 of 64), and 64 heads leave two waves of every decode
+    tile without a valid row. Keys are planted below the past length, where
+    the write phase does not touch them."""
+    kw = dict(_DSV3)
+    kw.update(num_heads=64, past=[300, 700], new=[1, 1], block_size=16, scale=1.0, dtype=dtype,
+              cache_std=0.25, key_std=0.25)
+    w = wl.build(_spec(name=f"score_jump_{dtype}", **kw))
+    H, hs, nr = 64, 576, 512
+    q = orc.widen(w["query"], dtype).reshape(-1, H, hs)
+    cache = w["key_cache"]
+    flat = cache.reshape(-1, hs)
+    bs = cache.shape[1]
+    cum, bt = w["cumulative_sequence_length"], w["block_table"]
+    for b, (h, j) in enumerate([(37, 250), (5, 611)]):
+        assert j < w["past_seqlens"][b]
+        slot = int(bt[b, j // bs]) * bs + j % bs
+        flat[slot, :nr] = wl.to_storage_bits((0.25 * q[cum[b], h, :nr]).astype(np.float32), dtype)
+    w["key_cache"] = flat.reshape(cache.shape)
+    ref_cache, ref_out = parity.oracle(w)
+    # One workgroup per query tile puts each planted key in a later tile of
+    # its piece (the case that needs the second pass); the automatic split
+    # spreads these few tiles one per piece and checks the combine with them.
+    for split_kv in (False, True):
+        d, before = _run(w, split_kv=split_kv)
+        parity.check_write(w, d.cache_bits(), ref_cache, before)
+        parity.check_output(dtype, d.output_f64(), ref_out, what=f"score_jump_{dtype} split_kv={split_kv}")
+
+
 def test_first_token_and_window0_exact():
     """A token that sees only itself outputs its own value row, bit for bit."""
     torch = _torch()
