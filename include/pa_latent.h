@@ -124,8 +124,8 @@ pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* di
  * Bytes of device workspace pa_latent_attention needs for these attrs/dims on
  * `device` (a HIP device ordinal). The workspace holds the on-device work
  * schedule and the split-KV partial results (float32 running max and
- * denominator per row, and the piece's normalised output row in the output
- * type). The result depends only on the
+ * denominator per row, and the piece's normalised output row: bfloat16 for
+ * bfloat16 outputs, float32 for float16 ones). The result depends only on the
  * arguments and the device's compute-unit count; it is written to *bytes.
  */
 pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
@@ -170,8 +170,9 @@ pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims
  * spread evenly over the device's compute units, long key ranges split and
  * merged by a log-sum-exp combine); split_kv == 0 gives every query tile to a
  * single workgroup (no partial results, no combine). The two agree up to
- * rounding (float32 accumulation order, and each piece's output rounded to
- * the output type before the combine); tests use this to check the combine.
+ * rounding (float32 accumulation order; with bfloat16 outputs each piece's
+ * output is rounded to bfloat16 before the combine); tests use this to check
+ * the combine.
  */
 pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
                                      pa_dtype dtype, const void* query, const void* key_cache,

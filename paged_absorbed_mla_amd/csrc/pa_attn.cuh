@@ -38,8 +38,9 @@
 //   * Work split (flash-decoding): an on-device scheduler lays the KV tiles of
 //     all query tiles end to end and gives every workgroup an equal share.
 //     A query tile whose tiles span several workgroups gets one partial per
-//     piece (float32 max and denominator, normalised output in the output
-//     type), merged by the combine kernel with a log-sum-exp weighting.
+//     piece (float32 max and denominator, normalised output: bfloat16 for
+//     bfloat16 outputs, float32 for float16 ones), merged by the combine
+//     kernel with a log-sum-exp weighting.
 #pragma once
 
 #include <type_traits>
@@ -75,9 +76,9 @@ struct AttnParams {
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
   const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
-  uint16_t* part_o;         // partial outputs acc / l in the output type: slot s, row r at s * part_slot + r * part_row
+  void* part_o;             // partial outputs acc / l (element type PartT<DT>): slot s, row r at s * part_slot + r * part_row
   int64_t part_slot;        // elements between slots (padded: not a power of two)
-  int part_row;             // elements between rows (VHSP + 8)
+  int part_row;             // elements between rows (VHSP + 16 bytes)
   const uint16_t* qrot;     // [T * H][rd]: query rotary channels after RoPE (four-wave 576 kernel)
   int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
@@ -87,6 +88,39 @@ struct AttnParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Element type of the split-KV partial outputs. bfloat16 outputs keep them in
+// bfloat16: a second rounding (half an ulp, 2^-8 relative at most) stays well
+// inside that type's output tolerance. float16 outputs keep them in float32:
+// the float16 tolerance is about one rounding of an output near 4, with no
+// room for a second.
+template <typename DT> struct PartF32 : std::false_type {};
+template <> struct PartF32<F16> : std::true_type {};
+
+// Eight normalised channels of a row into a partial slot.
+template <typename DT>
+__device__ __forceinline__ void store_part8(void* part, int64_t off, const float (&x)[8]) {
+  if constexpr (PartF32<DT>::value) {
+    float* d = (float*)part + off;
+    *(f32x4_t*)d = f32x4_t{x[0], x[1], x[2], x[3]};
+    *(f32x4_t*)(d + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
+  } else {
+    *(u32x4_t*)((uint16_t*)part + off) = pack8<DT>(x);
+  }
+}
+
+// Eight channels of a partial slot, widened to float32.
+template <typename DT>
+__device__ __forceinline__ void load_part8(const void* part, int64_t off, float (&x)[8]) {
+  if constexpr (PartF32<DT>::value) {
+    const f32x4_t a = *(const f32x4_t*)((const float*)part + off);
+    const f32x4_t b = *(const f32x4_t*)((const float*)part + off + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { x[k] = a[k]; x[4 + k] = b[k]; }
+  } else {
+    unpack8<DT>(*(const u32x4_t*)((const uint16_t*)part + off), x);
+  }
+}
 
 // Chunk swizzle of LDS row `key`: period 16 in the key, so rows 16 apart share
 // it and their addresses differ by a compile-time constant. Rows k and k + 8
@@ -602,14 +636,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     // A whole query tile writes its output rows. A split-KV piece writes its
-    // own normalised output acc / l, rounded to the output type, into its
-    // partial slot (rows padded to VHSP channels) and (m, l) in float32; the
-    // combine merges the pieces.
+    // own normalised output acc / l into its partial slot (element type
+    // PartT, rows padded to VHSP channels) and (m, l) in float32; the combine
+    // merges the pieces.
     if (row_ok) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-      uint16_t* orow;
       if (whole) {
-        orow = p.out + qrow * p.vhs;
+        uint16_t* const orow = p.out + qrow * p.vhs;
+        if (p.vhs == VHSP) {
+          // Lane writes channels mt*32 + hi*4 + 8*grp .. + 3 of its row: one
+          // base address, immediate offsets.
+          uint16_t* ob = orow + hi * 4;
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+              const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
+              const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
+              const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
+              const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
+              *(u32x2_t*)(ob + mt * 32 + 8 * grp) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+            }
+          }
+        } else {
+          for (int mt = 0; mt < NMT; ++mt) {
+            for (int e = 0; e < 16; ++e) {
+              const int c = mt * 32 + hi * 4 + 8 * (e >> 2) + (e & 3);
+              if (c < p.vhs) orow[c] = (uint16_t)DT::from_f32(st.o[mt][e] * inv);
+            }
+          }
+        }
       } else {
         const int64_t slot = (int64_t)t.part_base + (wr - t.w_first);
         if (hi == 0) {
@@ -617,28 +673,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           ml[0] = st.m_run;
           ml[1] = l_tot;
         }
-        orow = p.part_o + slot * p.part_slot + (int64_t)rloc * p.part_row;
-      }
-      if (!whole || p.vhs == VHSP) {
-        // Lane writes channels mt*32 + hi*4 + 8*grp .. + 3 of its row: one base
-        // address, immediate offsets.
-        uint16_t* ob = orow + hi * 4;
+        const int64_t prow = slot * p.part_slot + (int64_t)rloc * p.part_row + hi * 4;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
-            const uint32_t e0 = DT::from_f32(st.o[mt][4 * grp + 0] * inv);
-            const uint32_t e1 = DT::from_f32(st.o[mt][4 * grp + 1] * inv);
-            const uint32_t e2 = DT::from_f32(st.o[mt][4 * grp + 2] * inv);
-            const uint32_t e3 = DT::from_f32(st.o[mt][4 * grp + 3] * inv);
-            *(u32x2_t*)(ob + mt * 32 + 8 * grp) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-          }
-        }
-      } else {
-        for (int mt = 0; mt < NMT; ++mt) {
-          for (int e = 0; e < 16; ++e) {
-            const int c = mt * 32 + hi * 4 + 8 * (e >> 2) + (e & 3);
-            if (c < p.vhs) orow[c] = (uint16_t)DT::from_f32(st.o[mt][e] * inv);
+            const int64_t off = prow + mt * 32 + 8 * grp;
+            const float x0 = st.o[mt][4 * grp + 0] * inv, x1 = st.o[mt][4 * grp + 1] * inv;
+            const float x2 = st.o[mt][4 * grp + 2] * inv, x3 = st.o[mt][4 * grp + 3] * inv;
+            if constexpr (PartF32<DT>::value) {
+              *(f32x4_t*)((float*)p.part_o + off) = f32x4_t{x0, x1, x2, x3};
+            } else {
+              *(u32x2_t*)((uint16_t*)p.part_o + off) =
+                  u32x2_t{DT::from_f32(x0) | (DT::from_f32(x1) << 16), DT::from_f32(x2) | (DT::from_f32(x3) << 16)};
+            }
           }
         }
       }
@@ -650,8 +698,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 }
 
 // Merge the partials of every query tile that several workgroups processed.
-// Piece i of a row holds its normalised output o_i = acc_i / l_i (output
-// type), its running max m_i (log2 domain) and denominator l_i; with
+// Piece i of a row holds its normalised output o_i = acc_i / l_i (bfloat16
+// for bfloat16 outputs, else float32: PartF32), its running max m_i (log2
+// domain) and denominator l_i; with
 // M = max_i m_i and c_i = 2^(m_i - M) l_i, out = sum_i c_i o_i / sum_i c_i
 // (float32), rounded to nearest even.
 // Grid: (query tiles, RW / kCombineRows) of 256 threads. TPR threads share a
@@ -680,33 +729,30 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   if (r0 >= t.nrows) return;
   const int nq = t.npieces;
   const int cum_b = ld_uniform(p.cumseq + t.b);
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
     const int r = r0 + rr;
     if (r >= t.nrows) continue;
     const int c0 = (threadIdx.x % TPR) * 8;                 // channel of group 0; group v at c0 + 8 TPR v
     if (c0 >= p.vhs) continue;
     const float* ml = p.part_ml + ((int64_t)t.part_base * RW + r) * 2;   // piece q at + q * RW * 2
-    // Piece q's slice at + q * part_slot (16-byte aligned: row and slot strides are multiples of 8 elements).
-    const uint16_t* po0 = p.part_o + (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;
+    // Piece q's slice at element + q * part_slot (16-byte aligned: row and
+    // slot strides are multiples of 16 bytes).
+    const int64_t po0 = (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;
     float acc[NV][8];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
-    auto add = [&](float wgt, const u32x4_t (&a)[NV]) {
+    auto add = [&](float wgt, const float (&a)[NV][8]) {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float x[8];
-        unpack8<DT>(a[v], x);
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[v][e] += wgt * x[e];
-      }
+        for (int e = 0; e < 8; ++e) acc[v][e] += wgt * a[v][e];
     };
     if (nq <= QA) {
       // Up to QA pieces (the usual case): the (m, l) pairs and every slice
       // load are issued together, one memory round trip per row.
-      u32x4_t a[QA][NV];
+      float a[QA][NV][8];
       float m[QA], l[QA];
 #pragma unroll
       for (int k = 0; k < QA; ++k) {
@@ -714,9 +760,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
         const int q = ok ? k : 0;
         m[k] = ok ? ml[(int64_t)q * RW * 2] : -INFINITY;
         l[k] = ok ? ml[(int64_t)q * RW * 2 + 1] : 0.0f;
-        const u32x4_t* src = (const u32x4_t*)(po0 + (int64_t)q * p.part_slot);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) a[k][v] = ok ? src[v * TPR] : zero4;
+        for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po0 + (int64_t)q * p.part_slot + 8 * TPR * v, a[k][v]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -753,15 +798,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       const float inv = den > 0.0f ? 1.0f / den : 0.0f;
       // Weighted sum of the row slices.
       for (int q0 = 0; q0 < nq; q0 += QA) {
-        u32x4_t a[QA][NV];
+        float a[QA][NV][8];
         float wq[QA];
 #pragma unroll
         for (int k = 0; k < QA; ++k) {
           const bool ok = q0 + k < nq;
           const int q = ok ? q0 + k : q0;
-          const u32x4_t* src = (const u32x4_t*)(po0 + (int64_t)q * p.part_slot);
 #pragma unroll
-          for (int v = 0; v < NV; ++v) a[k][v] = src[v * TPR];
+          for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po0 + (int64_t)q * p.part_slot + 8 * TPR * v, a[k][v]);
           const float m = ml[(int64_t)q * RW * 2], l = ml[(int64_t)q * RW * 2 + 1];
           wq[k] = (!ok || m == -INFINITY) ? 0.0f : fast_exp2(m - mx) * l * inv;
         }

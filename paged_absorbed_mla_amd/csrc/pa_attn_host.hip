@@ -346,7 +346,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   cfg->piece_units = 2;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 8; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 12; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
@@ -395,11 +395,13 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_sched = off; off = align256(off + (size_t)L.sched_ints * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
-  // Partial outputs (16-bit, the output type): rows padded by 16 bytes and
-  // slots by 128 bytes so concurrent pieces do not sit at power-of-two strides.
-  L.part_row = cfg.vhsp + 8;
-  L.part_slot = (int64_t)RW * L.part_row + 64;
-  L.off_part_o = off; off = align256(off + (size_t)L.part_cap * L.part_slot * sizeof(uint16_t));
+  // Partial outputs (bfloat16 for bfloat16 outputs, float32 for float16
+  // ones; PartF32 in the kernels): rows padded by 16 bytes and slots by 256
+  // bytes so concurrent pieces do not sit at power-of-two strides.
+  const int pe = g.dtype == 10 ? 4 : 2;   // partial element bytes
+  L.part_row = cfg.vhsp + 16 / pe;
+  L.part_slot = (int64_t)RW * L.part_row + 256 / pe;
+  L.off_part_o = off; off = align256(off + (size_t)L.part_cap * L.part_slot * pe);
   L.off_qrot = 0;
   if (cfg.wide == 2 && g.do_rotary) {
     L.off_qrot = off;
@@ -468,7 +470,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.mt = sp.mt;
   ap.zero16 = (const uint16_t*)sp.zero16;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
-  ap.part_o = (uint16_t*)(wsb + ws.off_part_o);
+  ap.part_o = (void*)(wsb + ws.off_part_o);
   ap.part_slot = ws.part_slot;
   ap.part_row = ws.part_row;
   ap.qrot = sp.qrot;

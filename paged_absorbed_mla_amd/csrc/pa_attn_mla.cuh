@@ -827,8 +827,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             inv_r[k] = lr > 0.0f ? 1.0f / lr : 0.0f;
           }
         }
-        uint16_t* const dst0 = whole ? p.out + (orow0 + r0f) * VHSP + cg
-                                     : p.part_o + slot * p.part_slot + (int64_t)r0f * p.part_row + cg;
+        // Element offsets of row r0f: output (whole tile) or partial slot.
+        const int64_t dst0 = whole ? (orow0 + r0f) * VHSP + cg : slot * p.part_slot + (int64_t)r0f * p.part_row + cg;
         const int64_t dstep = whole ? (int64_t)RSTEP * VHSP : (int64_t)RSTEP * p.part_row;
         const float* const src0 = ost + r0f * ORS + sc;
 #pragma unroll
@@ -844,7 +844,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const float inv = inv_r[k0 + k];
             const float x[8] = {v0[k][0] * inv, v0[k][1] * inv, v0[k][2] * inv, v0[k][3] * inv,
                                 v1[k][0] * inv, v1[k][1] * inv, v1[k][2] * inv, v1[k][3] * inv};
-            *(u32x4_t*)(dst0 + (k0 + k) * dstep) = pack8<DT>(x);
+            if (whole) *(u32x4_t*)(p.out + dst0 + (k0 + k) * dstep) = pack8<DT>(x);
+            else store_part8<DT>(p.part_o, dst0 + (k0 + k) * dstep, x);
           }
         }
       } else for (int idx = etid; idx < RW * C8; idx += NW * 64) {
@@ -859,12 +860,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float x[8] = {v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv,
                             v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv};
         // Output row, or the piece's partial row (padded to VHSP channels).
-        uint16_t* dst = whole ? p.out + (orow0 + r) * p.vhs + cg
-                              : p.part_o + slot * p.part_slot + (int64_t)r * p.part_row + cg;
-        if (!whole || (cg + 8 <= p.vhs && (p.vhs & 7) == 0)) {
-          *(u32x4_t*)dst = pack8<DT>(x);
+        if (!whole) {
+          store_part8<DT>(p.part_o, slot * p.part_slot + (int64_t)r * p.part_row + cg, x);
         } else {
-          for (int k = 0; k < 8 && cg + k < p.vhs; ++k) dst[k] = (uint16_t)DT::from_f32(x[k]);
+          uint16_t* dst = p.out + (orow0 + r) * p.vhs + cg;
+          if (cg + 8 <= p.vhs && (p.vhs & 7) == 0) {
+            *(u32x4_t*)dst = pack8<DT>(x);
+          } else {
+            for (int k = 0; k < 8 && cg + k < p.vhs; ++k) dst[k] = (uint16_t)DT::from_f32(x[k]);
+          }
         }
       }
       lds_barrier();     // staging area free again

@@ -48,8 +48,8 @@ struct WsLayout {
   size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_zero, off_part_ml, off_part_o;
   int64_t sched_ints;   // scheduler scratch (int32) when it does not fit its LDS
   size_t off_qrot;      // rotated query channels [T * H][rd] (0: none)
-  int64_t part_slot;    // 16-bit elements between partial-result slots
-  int part_row;         // 16-bit elements between partial-result rows
+  int64_t part_slot;    // partial-output elements between slots (bf16 or f32, by output type)
+  int part_row;         // partial-output elements between rows
   size_t total;
 };
 
