@@ -79,7 +79,7 @@ struct AttnParams {
   void* part_o;             // partial outputs acc / l (element type PartT<DT>): slot s, row r at s * part_slot + r * part_row
   int64_t part_slot;        // elements between slots (padded: not a power of two)
   int part_row;             // elements between rows (VHSP + 16 bytes)
-  const uint16_t* qrot;     // [T * H][rd]: query rotary channels after RoPE (four-wave 576 kernel)
+  const uint16_t* qfrag;    // [T * H][HSP]: RoPE'd query in fragment order (four-wave 576 kernel)
   int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H, hs, vhs, bs_log2, MB;

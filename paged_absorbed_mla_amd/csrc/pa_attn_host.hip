@@ -21,12 +21,13 @@ struct SchedParams {
   const int32_t* past;
   int B, H, RW, KT, window, grid, split_kv;
   int piece_units;   // virtual KV tiles charged at the start of every query tile
-  // Query RoPE pre-pass (blocks 1..): qrot[t * H + h][0 : rd] = RoPE of the
-  // query channels [ro, ro + rd) of (t, h), rounded to the storage type.
+  // Query pre-pass (blocks 1.., four-wave 576 kernel): the query with RoPE
+  // applied, in the attention kernel's fragment order (qfrag, [T * H][hsp]).
   const uint16_t* query;
   const uint16_t* cos_t;
   const uint16_t* sin_t;
-  uint16_t* qrot;
+  uint16_t* qfrag;
+  int hsp;
   int64_t T, prow;
   int hs, ro, rd, interleaved, dtype;
   int64_t max_mtiles, part_cap;
@@ -87,24 +88,44 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
   return lo;
 }
 
-// Blocks 1.. of the schedule launch: RoPE of the query's rotary channels into
-// the workspace, one 8-channel chunk per thread (float32 math, nearest-even
-// rounding; same rotation as the write phase applies to key rows). `cum` and
-// `pst` are cumulative_sequence_length and past_seqlens (staged in LDS when
-// they fit).
+// Blocks 1.. of the schedule launch: the query in the four-wave kernel's
+// fragment order, RoPE applied (float32 math, nearest-even rounding; the same
+// rotation the write phase applies to key rows). Each sequence's rows are cut
+// into blocks of 32 (the rows one wave holds); a block whose first row is R0
+// and which has nv rows keeps the span [R0, R0 + nv) * hsp and stores 8-channel
+// chunk c of its row l (zero past hs) at chunk c * nv + l, so the wave reads
+// k-step s (chunks 2 s and 2 s + 1 of every row) as one contiguous run of
+// 32 nv bytes. One chunk per thread, threads in destination order (coalesced
+// stores). `cum` and `pst` are cumulative_sequence_length and past_seqlens
+// (staged in LDS when they fit).
 template <typename DT>
-__device__ void query_rope_chunk(const SchedParams& p, int64_t idx, const int32_t* cum, const int32_t* pst) {
-  const int cpr = p.rd >> 3;                      // rotary chunks per row
-  const int64_t row = idx / cpr;                  // t * H + h
-  const int c0 = p.ro + (int)(idx - row * cpr) * 8;
-  const int64_t t = row / p.H;
-  const uint16_t* qrow = p.query + row * p.hs;
-  float x[8];
-  unpack8<DT>(*(const u32x4_t*)(qrow + c0), x);
-  const int b = find_seq(cum, p.B, t);
-  const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
-  rope_chunk<DT>(x, qrow, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
-  *(u32x4_t*)(p.qrot + row * p.rd + (c0 - p.ro)) = pack8<DT>(x);
+__device__ void query_frag_chunk(const SchedParams& p, int64_t d, const int32_t* cum, const int32_t* pst) {
+  const int cpr = p.hsp >> 3;                          // chunks per row
+  const int64_t Rg = d / cpr;                          // a row of the block holding chunk d
+  const int b = find_seq(cum, p.B, Rg / p.H);
+  const int64_t s0 = (int64_t)cum[b] * p.H;            // the sequence's first row
+  const int64_t rows_b = (int64_t)(cum[b + 1] - cum[b]) * p.H;
+  const int64_t k32 = (Rg - s0) & ~(int64_t)31;        // block's first row within the sequence
+  const int64_t R0 = s0 + k32;
+  const int nv = (int)min((int64_t)32, rows_b - k32);
+  const int local = (int)(d - R0 * cpr);
+  const int c = local / nv;
+  const int64_t R = R0 + (local - c * nv);
+  const int c0 = c * 8;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (c0 < p.hs) {
+    const uint16_t* qrow = p.query + R * p.hs;
+    v = *(const u32x4_t*)(qrow + c0);
+    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd) {
+      float x[8];
+      unpack8<DT>(v, x);
+      const int64_t t = R / p.H;
+      const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
+      rope_chunk<DT>(x, qrow, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
+      v = pack8<DT>(x);
+    }
+  }
+  *(u32x4_t*)(p.qfrag + d * 8) = v;
 }
 
 // Block 0 of the schedule launch builds the whole schedule in working arrays
@@ -289,11 +310,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     }
     const int32_t* cum = staged ? lds_arr : p.cumseq;
     const int32_t* pst = staged ? lds_arr + p.B + 1 : p.past;
-    const int64_t n = p.T * p.H * (p.rd >> 3);
+    const int64_t n = p.T * p.H * (p.hsp >> 3);
     const int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x;
     if (idx < n) {
-      if (p.dtype == 16) query_rope_chunk<BF16>(p, idx, cum, pst);
-      else query_rope_chunk<F16>(p, idx, cum, pst);
+      if (p.dtype == 16) query_frag_chunk<BF16>(p, idx, cum, pst);
+      else query_frag_chunk<F16>(p, idx, cum, pst);
     }
     return;
   }
@@ -402,10 +423,10 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.part_row = cfg.vhsp + 16 / pe;
   L.part_slot = (int64_t)RW * L.part_row + 256 / pe;
   L.off_part_o = off; off = align256(off + (size_t)L.part_cap * L.part_slot * pe);
-  L.off_qrot = 0;
-  if (cfg.wide == 2 && g.do_rotary) {
-    L.off_qrot = off;
-    off = align256(off + (size_t)(g.T * g.H * g.rd) * 2);
+  L.off_qfrag = 0;
+  if (cfg.wide == 2) {
+    L.off_qfrag = off;
+    off = align256(off + (size_t)(g.T * g.H * cfg.hsp) * 2);
   }
   L.total = off;
   return L;
@@ -441,15 +462,16 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.query = (const uint16_t*)query;
   sp.cos_t = (const uint16_t*)cos_t;
   sp.sin_t = (const uint16_t*)sin_t;
-  sp.qrot = ws.off_qrot ? (uint16_t*)(wsb + ws.off_qrot) : nullptr;
+  sp.qfrag = ws.off_qfrag ? (uint16_t*)(wsb + ws.off_qfrag) : nullptr;
+  sp.hsp = cfg.hsp;
   sp.T = g.T;
   sp.prow = g.do_rotary ? g.P : 1;
   sp.hs = g.hs;
   sp.ro = g.ro;
-  sp.rd = g.rd;
+  sp.rd = g.do_rotary ? g.rd : 0;   // 0: no rotary channels
   sp.interleaved = g.interleaved;
   sp.dtype = g.dtype;
-  const int64_t rope_chunks = sp.qrot ? g.T * g.H * (g.rd >> 3) : 0;
+  const int64_t rope_chunks = sp.qfrag ? g.T * g.H * (cfg.hsp >> 3) : 0;
   const int64_t rope_blocks = (rope_chunks + kSchedThreads - 1) / kSchedThreads;
   schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
@@ -473,7 +495,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.part_o = (void*)(wsb + ws.off_part_o);
   ap.part_slot = ws.part_slot;
   ap.part_row = ws.part_row;
-  ap.qrot = sp.qrot;
+  ap.qfrag = sp.qfrag;
   ap.nblk = g.NB;
   ap.prow = g.do_rotary ? g.P : 1;
   ap.H = g.H;

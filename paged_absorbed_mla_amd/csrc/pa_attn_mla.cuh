@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // This lane's query row (rows past the tile read row 0 of the tile and are
     // never stored; each row's softmax and output column are independent).
-    const int rloc = w * 32 + l32;
+    const int rloc = w * 32 + (fresh_lane() & 31);   // re-derived per piece: nothing lane-derived is kept in a spill slot
     const bool row_ok = rloc < t.nrows;
     const int R = t.row0 + (row_ok ? rloc : 0);
     const int tq = R / p.H;
@@ -571,47 +571,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int k = 0; k < NB - 2; ++k) issue(tile_a + k, k, block_of(min(tile_a + k, tile_b - 1)));
 
-    // Query fragments: k-step s holds channels 16 s + 8 hi .. + 8 of the row.
-    // The tile's rows are consecutive in `query`; one buffer descriptor covers
-    // exactly them (from the tile's first row) and each lane's row and chunk
-    // go in the per-lane offset. Rows past the tile read the tile's row 0, so
-    // every read stays inside the tile; chunks past hs take an out-of-range
-    // offset and read zeros.
+    // Query fragments (k-step s holds channels 16 s + 8 hi .. + 8 of the row),
+    // from the copy the schedule launch wrote in fragment
+    // order with RoPE applied (qfrag): the wave's 32-row block (nv rows) holds
+    // 8-channel chunk c of its row l at chunk c * nv + l, so k-step s of lane
+    // (l, hi) is chunk (2 s + hi) nv + l and every load reads one contiguous
+    // run. A wave with no row of the tile reads the tile's first block; lanes
+    // past their block's rows read its row 0 (they never vote or store). One
+    // descriptor covers exactly the block read.
     MlaState<HSP, VHSP> st;
     const int64_t trow0 = (int64_t)cum_b * p.H + t.row0;   // first query row of the tile
     {
-      // hs pinned to a scalar register: a value the compiler rematerialises
-      // from a spill slot here would need a vmcnt wait, and since it does not
-      // see the tile copies above that wait would drain them before the query
-      // loads go out.
-      int qhs = p.hs;
-      asm volatile("" : "+s"(qhs));
-      const u32x4_t qrs = rsrc_words_u(p.query + trow0 * qhs, (uint32_t)(t.nrows * qhs * 2));
+      const int nvw = min(32, t.nrows - 32 * w);            // the wave's own rows
+      const int nvb = nvw > 0 ? nvw : min(32, t.nrows);     // rows of the block read
+      const int64_t brow = trow0 + (nvw > 0 ? 32 * w : 0);  // its first row
+      const u32x4_t qrs = rsrc_words_u(p.qfrag + brow * HSP, (uint32_t)(nvb * HSP * 2));
       const int ln = opaque_lane();
-      const int lr = (32 * w + (ln & 31)) < t.nrows ? 32 * w + (ln & 31) : 0;
-      const uint32_t qbase = (uint32_t)(lr * qhs * 2);
-      const int h8 = (ln >> 5) * 8;
+      const int l = (ln & 31) < nvb ? (ln & 31) : 0;
+      const uint32_t lb = (uint32_t)((((ln >> 5) * nvb) + l) * 16);
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int c0 = 16 * s + h8;
-        st.qf[s] = buffer_load_b128(qrs, c0 < qhs ? qbase + (uint32_t)(c0 * 2) : kOutOfRange);
-      }
-      // Rotary chunks come from the RoPE'd copy the schedule launch wrote
-      // (qrot, rd channels per row); the test on the k-step is uniform and the
-      // geometry is opaque so nothing is hoisted out of the piece loop.
-      if (p.do_rotary) {
-        int ro = p.ro, rd = p.rd;
-        asm volatile("" : "+s"(ro), "+s"(rd));
-        const u32x4_t rrs = rsrc_words_u(p.qrot + trow0 * rd, (uint32_t)(t.nrows * rd * 2));
-        const uint32_t rbase = (uint32_t)(lr * rd * 2);
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          if (16 * s + 16 > ro && 16 * s < ro + rd) {
-            const int c0 = 16 * s + h8;
-            if (c0 >= ro && c0 < ro + rd) st.qf[s] = buffer_load_b128(rrs, rbase + (uint32_t)((c0 - ro) * 2));
-          }
-        }
-      }
+      for (int s = 0; s < NKS; ++s) st.qf[s] = buffer_load_b128(qrs, lb + (uint32_t)(s * 32 * nvb));
     }
 
     // The first two KV tiles of the piece are already in flight (issued
