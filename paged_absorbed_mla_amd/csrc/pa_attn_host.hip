@@ -95,37 +95,67 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
 // and which has nv rows keeps the span [R0, R0 + nv) * hsp and stores 8-channel
 // chunk c of its row l (zero past hs) at chunk c * nv + l, so the wave reads
 // k-step s (chunks 2 s and 2 s + 1 of every row) as one contiguous run of
-// 32 nv bytes. One chunk per thread, threads in destination order (coalesced
-// stores). `cum` and `pst` are cumulative_sequence_length and past_seqlens
-// (staged in LDS when they fit).
-template <typename DT>
-__device__ void query_frag_chunk(const SchedParams& p, int64_t d, const int32_t* cum, const int32_t* pst) {
+// 32 nv bytes. Threads take chunks in destination order (coalesced stores).
+// `cum` and `pst` are cumulative_sequence_length and past_seqlens (staged in
+// LDS when they fit).
+//
+// Where chunk d of the fragment-ordered copy comes from: query row R and
+// channel c0 (the chunk's first), and the row's sequence b.
+struct FragSrc {
+  int64_t R;
+  int c0, b;
+};
+
+__device__ __forceinline__ FragSrc frag_source(const SchedParams& p, int64_t d, const int32_t* cum) {
   const int cpr = p.hsp >> 3;                          // chunks per row
   const int64_t Rg = d / cpr;                          // a row of the block holding chunk d
-  const int b = find_seq(cum, p.B, Rg / p.H);
-  const int64_t s0 = (int64_t)cum[b] * p.H;            // the sequence's first row
-  const int64_t rows_b = (int64_t)(cum[b + 1] - cum[b]) * p.H;
+  FragSrc f;
+  f.b = find_seq(cum, p.B, Rg / p.H);
+  const int64_t s0 = (int64_t)cum[f.b] * p.H;          // the sequence's first row
+  const int64_t rows_b = (int64_t)(cum[f.b + 1] - cum[f.b]) * p.H;
   const int64_t k32 = (Rg - s0) & ~(int64_t)31;        // block's first row within the sequence
   const int64_t R0 = s0 + k32;
   const int nv = (int)min((int64_t)32, rows_b - k32);
   const int local = (int)(d - R0 * cpr);
   const int c = local / nv;
-  const int64_t R = R0 + (local - c * nv);
-  const int c0 = c * 8;
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (c0 < p.hs) {
-    const uint16_t* qrow = p.query + R * p.hs;
-    v = *(const u32x4_t*)(qrow + c0);
-    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd) {
-      float x[8];
-      unpack8<DT>(v, x);
-      const int64_t t = R / p.H;
-      const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
-      rope_chunk<DT>(x, qrow, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
-      v = pack8<DT>(x);
+  f.R = R0 + (local - c * nv);
+  f.c0 = c * 8;
+  return f;
+}
+
+// Chunks d0, d0 + stride, ... (KB of them, those below n) of the copy: the
+// plain loads of the batch go out together, then rotary chunks are rotated
+// and every chunk is stored.
+template <typename DT, int KB>
+__device__ __forceinline__ void query_frag_batch(const SchedParams& p, int64_t d0, int64_t stride, int64_t n,
+                                                 const int32_t* cum, const int32_t* pst) {
+  FragSrc f[KB];
+  u32x4_t v[KB];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const int64_t d = d0 + k * stride;
+    v[k] = u32x4_t{0u, 0u, 0u, 0u};
+    if (d < n) {
+      f[k] = frag_source(p, d, cum);
+      if (f[k].c0 < p.hs) v[k] = *(const u32x4_t*)(p.query + f[k].R * p.hs + f[k].c0);
     }
   }
-  *(u32x4_t*)(p.qfrag + d * 8) = v;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const int64_t d = d0 + k * stride;
+    if (d >= n) continue;
+    const int c0 = f[k].c0;
+    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd) {
+      const int b = f[k].b;
+      float x[8];
+      unpack8<DT>(v[k], x);
+      const int64_t t = f[k].R / p.H;
+      const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
+      rope_chunk<DT>(x, p.query + f[k].R * p.hs, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
+      v[k] = pack8<DT>(x);
+    }
+    *(u32x4_t*)(p.qfrag + d * 8) = v[k];
+  }
 }
 
 // Block 0 of the schedule launch builds the whole schedule in working arrays
@@ -310,11 +340,15 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     }
     const int32_t* cum = staged ? lds_arr : p.cumseq;
     const int32_t* pst = staged ? lds_arr + p.B + 1 : p.past;
+    // Grid-stride over the chunks: the launch holds few of these blocks (the
+    // LDS array sized for block 0 allows three per CU), each thread taking a
+    // chunk per stride.
+    constexpr int KB = 4;   // chunks per thread whose loads are in flight together
     const int64_t n = p.T * p.H * (p.hsp >> 3);
-    const int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x;
-    if (idx < n) {
-      if (p.dtype == 16) query_frag_chunk<BF16>(p, idx, cum, pst);
-      else query_frag_chunk<F16>(p, idx, cum, pst);
+    const int64_t stride = (int64_t)(gridDim.x - 1) * kSchedThreads;
+    for (int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x; idx < n; idx += KB * stride) {
+      if (p.dtype == 16) query_frag_batch<BF16, KB>(p, idx, stride, n, cum, pst);
+      else query_frag_batch<F16, KB>(p, idx, stride, n, cum, pst);
     }
     return;
   }
@@ -471,8 +505,11 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.rd = g.do_rotary ? g.rd : 0;   // 0: no rotary channels
   sp.interleaved = g.interleaved;
   sp.dtype = g.dtype;
+  // Query pre-pass blocks: at most kPrepassBlocks (two per compute unit of a
+  // 256-CU part; grid-stride loop).
+  constexpr int64_t kPrepassBlocks = 512;
   const int64_t rope_chunks = sp.qfrag ? g.T * g.H * (cfg.hsp >> 3) : 0;
-  const int64_t rope_blocks = (rope_chunks + kSchedThreads - 1) / kSchedThreads;
+  const int64_t rope_blocks = std::min<int64_t>((rope_chunks + kSchedThreads - 1) / kSchedThreads, kPrepassBlocks);
   schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
