@@ -401,7 +401,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   cfg->piece_units = 2;
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 12; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 10; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
