@@ -200,6 +200,14 @@ struct MlaState {
 template <typename DT> struct PRange;
 template <> struct PRange<BF16> { static constexpr float value = 64.0f; };
 template <> struct PRange<F16> { static constexpr float value = 15.0f; };
+// Headroom of a reference taken from a tile where the row sees at most four
+// keys (a window edge, the first keys of a sequence): the maximum of so few
+// scores sits well below the row's, so with float16's narrow range the
+// reference starts that many log2 units higher (the row's larger
+// probabilities stay near 1, inside float16's normal range). bfloat16 needs none.
+template <typename DT> struct PHead;
+template <> struct PHead<BF16> { static constexpr float value = 0.0f; };
+template <> struct PHead<F16> { static constexpr float value = 8.0f; };
 
 // ---- Tile steps of the software-pipelined loop ----
 // Iteration t queues the QK MFMAs of tile t (mla_qk), then runs the PV MFMAs
@@ -296,7 +304,6 @@ constexpr int kSmChunks = 12;
 template <typename DT, int HSP, int VHSP, int C>
 __device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm, int key0, int pos, int lo_row,
                                              bool full_tile, bool softcap_on, const AttnParams& p) {
-  const int hi = (threadIdx.x & 63) >> 5;
   // Scale fused into the exponent (no softcap, scale > 0): the maximum of the
   // raw scores times the scale is the maximum logit (rounding is monotone),
   // and each probability is 2^fma(s, scale, -reference). Otherwise step 0
@@ -318,6 +325,9 @@ __device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm,
   } else if constexpr (C == 1) {
     // mask (in place, only for a tile some row does not see whole) and tile max
     if (!full_tile) {
+      // Lane half re-derived here (a copy kept across the tile loop would sit
+      // in a spill slot).
+      const int hi = fresh_lane() >> 5;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = key0 + hi * 4 + (e & 3) + 8 * (e >> 2);
@@ -329,7 +339,14 @@ __device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm,
   } else if constexpr (C == 2) {
     const float tmax = fused ? max_xor32(sm.tmax) * p.scale_log2 : max_xor32(sm.tmax);
     st.m_seen = fmaxf(st.m_seen, tmax);
-    if (st.m_ref == -INFINITY) st.m_ref = tmax;
+    if (st.m_ref == -INFINITY) {
+      if constexpr (PHead<DT>::value > 0.0f) {
+        const int nvis = full_tile ? 32 : min(pos, key0 + 31) - max(lo_row, key0) + 1;   // row's visible keys
+        st.m_ref = tmax + (nvis <= 4 ? PHead<DT>::value : 0.0f);
+      } else {
+        st.m_ref = tmax;
+      }
+    }
     st.ovf |= tmax > st.m_ref + PRange<DT>::value;
     sm.m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
   } else if constexpr (C >= 3 && C < 11) {
