@@ -123,10 +123,12 @@ pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* di
 /*
  * Bytes of device workspace pa_latent_attention needs for these attrs/dims on
  * `device` (a HIP device ordinal). The workspace holds the on-device work
- * schedule and the split-KV partial results (float32 running max and
- * denominator per row, and the piece's normalised output row: bfloat16 for
- * bfloat16 outputs, float32 for float16 ones). The result depends only on the
- * arguments and the device's compute-unit count; it is written to *bytes.
+ * schedule; when head_size > 192 or v_head_size > 128, a RoPE'd copy of the
+ * query in the attention kernel's fragment order; and the split-KV partial
+ * results (float32 running max and denominator per row, and the piece's
+ * normalised output row: bfloat16 for bfloat16 outputs, float32 for float16
+ * ones). The result depends only on the arguments and the device's
+ * compute-unit count; it is written to *bytes.
  */
 pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
                                    pa_dtype dtype, int device, size_t* bytes);
