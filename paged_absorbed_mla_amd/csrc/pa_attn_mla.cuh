@@ -8,15 +8,20 @@
 // Design. One workgroup of four waves (one per SIMD, 512 registers each) owns a
 // 128-row query tile (row = token_in_sequence * H + head) and walks a
 // contiguous range of 32-key KV tiles:
-//   * Each wave owns 32 query rows for both products, so probabilities never
-//     leave registers: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16
-//     (tile_compute in pa_attn.cuh). The query (all HSP channels, 144
-//     registers) and the output accumulators (256 registers) stay resident
-//     for the whole piece.
-//   * The query is loaded straight into MFMA fragment registers; its rotary
-//     channels come already rotated from the schedule launch (a pre-pass over
-//     the T x H query rows that writes them to the workspace), so the whole
-//     query of a piece arrives in one batch of loads.
+//   * QK, row split: each wave keeps its 32 query rows (all HSP channels, 144
+//     registers) resident as MFMA fragments and forms S^T = K Q^T for them on
+//     v_mfma_f32_32x32x16. The query comes from a copy the schedule launch
+//     writes in fragment order with RoPE applied, so each load instruction
+//     reads one contiguous run.
+//   * PV, channel split: wave w accumulates O^T for all 128 rows but only value
+//     channels [128 w, 128 w + 128) (256 accumulator registers). Each wave
+//     writes its rows' probabilities of a tile once to a double-buffered LDS
+//     area in the S^T accumulator layout; every wave reads all of them and a
+//     quarter of V with transposing reads.
+//   * Fixed-reference softmax: a row's first tile with a visible key fixes
+//     its reference; the accumulators are never rescaled, and a score beyond
+//     the probability type's range above the reference sends the piece
+//     through a second pass with exact maxima.
 //   * KV tiles (32 latent rows, HSP channels, 36 KB) are copied from the paged
 //     cache into four LDS buffers with direct global->LDS loads; up to three
 //     tiles are in flight while one is computed. Wave w copies keys
@@ -27,8 +32,10 @@
 //   * One barrier per tile, ordering LDS only: each wave first waits for its
 //     own copies of the tile (vmcnt), so after the barrier the tile is
 //     complete and the buffer computed in the previous iteration is free.
-//   * The first KV tiles of a piece are issued right after the query loads and
-//     land while RoPE runs.
+//   * The first two KV tiles of a piece are issued before the query loads, so
+//     their latencies overlap.
+//   * Epilogue through LDS with coalesced stores: the output rows of a whole
+//     query tile, or the piece's partial slot for the split-KV combine.
 #pragma once
 
 #include "pa_attn.cuh"
