@@ -40,8 +40,10 @@
  *     rotary_rows > largest position. Violating them gives unspecified
  *     results, but no access leaves the caller's buffers: block ids are
  *     clamped into [0, num_blocks), rotary positions into [0, rotary_rows),
- *     slots past the cache are skipped like -1, and negative past lengths count
- *     as 0 when the key ranges are planned.
+ *     slots past the cache are skipped like -1, and the read phase plans its
+ *     work from sequence bounds clamped into [0, token_count] and made
+ *     non-decreasing and from past lengths clamped into
+ *     [0, max_blocks_per_seq * block_size].
  */
 #ifndef PA_LATENT_H
 #define PA_LATENT_H
@@ -122,13 +124,23 @@ pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* di
 
 /*
  * Bytes of device workspace pa_latent_attention needs for these attrs/dims on
- * `device` (a HIP device ordinal). The workspace holds the on-device work
- * schedule; when head_size > 192 or v_head_size > 128, a RoPE'd copy of the
- * query in the attention kernel's fragment order; and the split-KV partial
- * results (float32 running max and denominator per row, and the piece's
- * normalised output row: bfloat16 for bfloat16 outputs, float32 for float16
- * ones). The result depends only on the arguments and the device's
- * compute-unit count; it is written to *bytes.
+ * `device` (a HIP device ordinal). The op keeps transient compute scratch in
+ * a workspace its caller manages, apart from the KV cache, whose only owner
+ * is the caller's page authority (PR #1940 "PagedAttention v1 audit and MLA
+ * oracle", third commit: the EP's scratch is EP-managed workspace, not a
+ * second KV-cache authority; PR #1978 "Invariants held": no op-side
+ * allocation). The workspace holds the on-device work schedule; when
+ * head_size > 192 or v_head_size > 128, a RoPE'd copy of the query in the
+ * attention kernel's fragment order; and the split-KV partial results
+ * (float32 running max and denominator per row, and the piece's normalised
+ * output row: bfloat16 for bfloat16 outputs, float32 for float16 ones).
+ *
+ * The size depends only on the arguments and the device's compute-unit count.
+ * It is written to *bytes (0 on error) and the function returns a status like
+ * every other entry point, so an unsupported geometry is reported with a
+ * message rather than as a size of 0. Errors: PA_ERR_INVALID_ARGUMENT (NULL
+ * bytes, or the checks pa_latent_attention makes on attrs/dims),
+ * PA_ERR_NOT_IMPLEMENTED, PA_ERR_DEVICE (device query failed).
  */
 pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
                                    pa_dtype dtype, int device, size_t* bytes);
@@ -195,7 +207,11 @@ pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_late
 pa_status pa_latent_profile_next(void* before, void* after);
 
 /* Message of the last failed call on this thread ("" after a successful call).
- * Valid until the next call into this library on the same thread. */
+ * Valid until the next call into this library on the same thread. The op
+ * reports every rejection as a typed error carrying a message that names the
+ * offending attribute or input (docs.rs page, unsupported_reason and execute:
+ * NotImplemented / KernelFailed with a reason string); the status code is the
+ * type and this string the reason. */
 const char* pa_last_error(void);
 
 /* PA_LATENT_ABI_VERSION of the built library. */

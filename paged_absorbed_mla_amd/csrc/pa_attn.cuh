@@ -57,7 +57,9 @@ struct MTile {
   int32_t part_base;  // first partial slot, -1 when one workgroup covers the tile
   int32_t w_first;    // workgroup that processes the tile's first unit
   int32_t npieces;    // workgroups that process the tile
-  int32_t pad[3];
+  int32_t tok0;       // first token of sequence b (cumulative_sequence_length, clamped into [0, T])
+  int32_t past;       // past length of sequence b (clamped into [0, max_blocks_per_seq * block_size])
+  int32_t pad;
 };
 static_assert(sizeof(MTile) == 48, "MTile layout");
 
@@ -66,8 +68,6 @@ struct AttnParams {
   const uint16_t* cache;
   const uint16_t* cos_t;
   const uint16_t* sin_t;
-  const int32_t* cumseq;
-  const int32_t* past;
   const int32_t* bt;
   uint16_t* out;
   const int32_t* header;    // [0] work units U, [1] query tiles M, [2] partial slots used
@@ -264,7 +264,9 @@ __device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
   t.part_base = ld_uniform(q + 6);
   t.w_first = ld_uniform(q + 7);
   t.npieces = ld_uniform(q + 8);
-  t.pad[0] = t.pad[1] = t.pad[2] = 0;
+  t.tok0 = ld_uniform(q + 9);
+  t.past = ld_uniform(q + 10);
+  t.pad = 0;
   return t;
 }
 
@@ -500,8 +502,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     const int tile_b = tile_a + (ub - ua);
     const bool whole = (ua == t.unit0) && (ub == next0);
     const int b = t.b;
-    const int cum_b = ld_uniform(p.cumseq + b);
-    const int past_b = ld_uniform(p.past + b);
+    const int cum_b = t.tok0;
+    const int past_b = t.past;
 
     const int rloc = w * 32 + l32;
     const bool row_ok = rloc < t.nrows;
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           const int j = key0 + k;
           uint8_t* dst = dst0 + it * NT * 16;
           if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs) {
-            const int blkv = p.bt[(int64_t)b * p.MB + (j >> p.bs_log2)];
+            const int blkv = clamp_block(p.bt[(int64_t)b * p.MB + min(j >> p.bs_log2, p.MB - 1)], p.nblk);
             const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
             __builtin_amdgcn_global_load_lds(p.cache + row * p.hs + lc * 8, dst, 16, 0, 0);
           } else {
@@ -728,7 +730,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int r0 = blockIdx.y * kCombineRows;
   if (r0 >= t.nrows) return;
   const int nq = t.npieces;
-  const int cum_b = ld_uniform(p.cumseq + t.b);
+  const int cum_b = t.tok0;
   for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
     const int r = r0 + rr;
     if (r >= t.nrows) continue;

@@ -20,6 +20,7 @@ struct SchedParams {
   const int32_t* cumseq;
   const int32_t* past;
   int B, H, RW, KT, window, grid, split_kv;
+  int max_pos;       // max_blocks_per_seq * block_size: past lengths are clamped to it
   int piece_units;   // virtual KV tiles charged at the start of every query tile
   // Query pre-pass (blocks 1.., four-wave 576 kernel): the query with RoPE
   // applied, in the attention kernel's fragment order (qfrag, [T * H][hsp]).
@@ -77,6 +78,36 @@ __device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
   return carry;
 }
 
+// In-place inclusive prefix maximum of a[0, n) (LDS or global); every thread
+// of the block must call it.
+__device__ void block_inclusive_max_scan(int32_t* a, int64_t n) {
+  constexpr int NWV = kSchedThreads / 64;
+  __shared__ int32_t wave_max[NWV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t carry = INT32_MIN;
+  for (int64_t base = 0; base < n; base += kSchedThreads) {
+    const int64_t idx = base + threadIdx.x;
+    int32_t x = idx < n ? a[idx] : INT32_MIN;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d);
+      if (lane >= d) x = max(x, y);
+    }
+    if (lane == 63) wave_max[wave] = x;
+    __syncthreads();
+    int32_t before = carry, total = carry;
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) {
+      const int32_t wm = wave_max[k];
+      if (k < wave) before = max(before, wm);
+      total = max(total, wm);
+    }
+    if (idx < n) a[idx] = max(before, x);
+    carry = total;
+    __syncthreads();
+  }
+}
+
 // Workgroup w covers units [wg_range[w], wg_range[w+1]); the one that holds
 // unit u is the last w with wg_range[w] <= u.
 __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int u) {
@@ -101,6 +132,9 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
 //
 // Where chunk d of the fragment-ordered copy comes from: query row R and
 // channel c0 (the chunk's first), and the row's sequence b.
+// A chunk whose token the sequence bounds do not place inside [0, T) (only a
+// violated precondition does that) gets c0 = hsp: it is stored as zeros and
+// nothing is read for it.
 struct FragSrc {
   int64_t R;
   int c0, b;
@@ -109,14 +143,21 @@ struct FragSrc {
 __device__ __forceinline__ FragSrc frag_source(const SchedParams& p, int64_t d, const int32_t* cum) {
   const int cpr = p.hsp >> 3;                          // chunks per row
   const int64_t Rg = d / cpr;                          // a row of the block holding chunk d
+  const int64_t tok = Rg / p.H;
   FragSrc f;
-  f.b = find_seq(cum, p.B, Rg / p.H);
-  const int64_t s0 = (int64_t)cum[f.b] * p.H;          // the sequence's first row
-  const int64_t rows_b = (int64_t)(cum[f.b + 1] - cum[f.b]) * p.H;
+  f.b = find_seq(cum, p.B, tok);
+  const int64_t lo = cum[f.b], hi = cum[f.b + 1];
+  if (!(0 <= lo && lo <= tok && tok < hi && hi <= p.T)) {
+    f.R = 0;
+    f.c0 = p.hsp;
+    return f;
+  }
+  const int64_t s0 = lo * p.H;                         // the sequence's first row
+  const int64_t rows_b = (hi - lo) * p.H;
   const int64_t k32 = (Rg - s0) & ~(int64_t)31;        // block's first row within the sequence
   const int64_t R0 = s0 + k32;
-  const int nv = (int)min((int64_t)32, rows_b - k32);
-  const int local = (int)(d - R0 * cpr);
+  const int nv = (int)min((int64_t)32, rows_b - k32);  // >= 1: Rg lies in the block
+  const int local = (int)(d - R0 * cpr);               // in [0, nv * cpr)
   const int c = local / nv;
   f.R = R0 + (local - c * nv);
   f.c0 = c * 8;
@@ -145,7 +186,7 @@ __device__ __forceinline__ void query_frag_batch(const SchedParams& p, int64_t d
     const int64_t d = d0 + k * stride;
     if (d >= n) continue;
     const int c0 = f[k].c0;
-    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd) {
+    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd && c0 < p.hs) {
       const int b = f[k].b;
       float x[8];
       unpack8<DT>(v[k], x);
@@ -186,11 +227,16 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   int32_t* const tw0 = wt + p.grid;                    // [max_mtiles] first workgroup of each tile
   int32_t* const tw1 = tw0 + p.max_mtiles;             // [max_mtiles] last workgroup of each tile
 
+  // Sequence bounds and past lengths, forced into the ranges the
+  // preconditions promise (a violated precondition then gives unspecified
+  // values but no access outside the caller's buffers): bounds clamped into
+  // [0, T] and made non-decreasing, past lengths into [0, MB * bs].
   for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
-    cum[b] = p.cumseq[b];
-    if (b < p.B) pst[b] = max(p.past[b], 0);   // negative lengths (a violated precondition) count as 0
+    cum[b] = (int32_t)min(max((int64_t)p.cumseq[b], (int64_t)0), p.T);
+    if (b < p.B) pst[b] = min(max(p.past[b], 0), p.max_pos);
   }
   __syncthreads();
+  block_inclusive_max_scan(cum, p.B + 1);
   // A. query tiles per sequence, prefix-summed into sbase.
   const int64_t M_all = block_exclusive_scan(
       p.B,
@@ -307,7 +353,9 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     t.w_first = tw0[i];
     t.npieces = tw1[i] - tw0[i] + 1;
     t.part_base = np[i];
-    t.pad[0] = t.pad[1] = t.pad[2] = 0;
+    t.tok0 = cum[t.b];
+    t.past = pst[t.b];
+    t.pad = 0;
     p.mt[i] = t;
   }
   if (threadIdx.x == 0) {
@@ -317,7 +365,6 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     p.header[0] = (int32_t)U;
     p.header[1] = M;
     p.header[2] = (int32_t)slots;
-    p.header[3] = (slots > p.part_cap || M_all > p.max_mtiles) ? 1 : 0;
   }
   for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
     p.wg_range[w] = wr[w];
@@ -478,6 +525,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.cumseq = cumseq;
   sp.past = past;
   sp.B = g.B;
+  sp.max_pos = (int)((int64_t)g.MB * g.bs);
   sp.H = g.H;
   sp.RW = cfg.rows();
   sp.KT = cfg.kt;
@@ -519,8 +567,6 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.cache = (const uint16_t*)cache;
   ap.cos_t = (const uint16_t*)cos_t;
   ap.sin_t = (const uint16_t*)sin_t;
-  ap.cumseq = cumseq;
-  ap.past = past;
   ap.bt = block_table;
   ap.out = (uint16_t*)out;
   ap.header = sp.header;

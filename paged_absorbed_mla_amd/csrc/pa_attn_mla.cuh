@@ -507,8 +507,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tile_b = tile_a + (ub - ua);
     const bool whole = (ua == t.unit0) && (ub == next0);
     const int b = t.b;
-    const int cum_b = ld_uniform(p.cumseq + b);
-    const int past_b = ld_uniform(p.past + b);
+    const int cum_b = t.tok0;
+    const int past_b = t.past;
 
     // This lane's query row (rows past the tile read row 0 of the tile and are
     // never stored; each row's softmax and output column are independent).

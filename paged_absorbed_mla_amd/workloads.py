@@ -68,6 +68,7 @@ class Spec:
     rotary_offset: int
     block_size: int
     scale: float
+    has_scale: int = 1              # 0: no explicit scale (the op's default applies)
     softcap: float = 0.0
     local_window_size: int = -1
     do_rotary: int = 1
@@ -235,7 +236,7 @@ def build(spec: Spec, cfg: Optional[str] = None, scale_down: int = 1, poison: bo
         do_rotary=int(spec.do_rotary), rotary_interleaved=int(spec.rotary_interleaved),
         rotary_dim=rd, rotary_offset=spec.rotary_offset if rd > 0 else 0,
         local_window_size=int(spec.local_window_size), softcap=float(spec.softcap),
-        has_scale=1, scale=float(spec.scale),
+        has_scale=int(spec.has_scale), scale=float(spec.scale) if spec.has_scale else 0.0,
     )
     dims = dict(token_count=T, batch=B, max_blocks_per_seq=MB, num_blocks=NB, rotary_rows=P if rd > 0 else 0)
     return dict(

@@ -47,34 +47,40 @@ def check_write(w: dict, gpu_cache: np.ndarray, ref_cache: np.ndarray, before: n
         assert d.max() <= 1, f"rotary channels differ by {d.max()} ulp"
 
 
-def check_output(dtype: str, got: np.ndarray, ref: np.ndarray, rows=None, what=""):
-    if rows is not None:
-        got, ref = got[rows], ref[rows]
-    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+def errors(got: np.ndarray, ref: np.ndarray):
+    """(max-abs error, relative Frobenius error) of got against ref."""
     err = np.abs(got - ref)
     max_abs = float(err.max()) if err.size else 0.0
     den = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref)) / den if den > 0 else float(np.linalg.norm(got))
-    assert max_abs <= MAX_ABS[dtype], f"{what}: max-abs {max_abs:.3e} > {MAX_ABS[dtype]}"
-    assert rel <= REL_FRO[dtype], f"{what}: relative Frobenius {rel:.3e} > {REL_FRO[dtype]}"
-    # negative control: the same check must reject an all-zero output
-    zero_rel = 1.0 if den > 0 else 0.0
-    assert den == 0 or zero_rel > REL_FRO[dtype]
     return max_abs, rel
 
 
-def sample_tokens(w: dict, n: int, seed: int = 0) -> np.ndarray:
-    """Sampled tokens: first and last token of the batch, last token of each of a few
-    sequences, plus random ones."""
-    T = w["dims"]["token_count"]
-    rng = np.random.default_rng(seed)
-    cum = w["cumulative_sequence_length"]
-    picks = {0, T - 1}
-    for b in rng.choice(len(cum) - 1, size=min(n, len(cum) - 1), replace=False):
-        if cum[b + 1] > cum[b]:
-            picks.add(int(cum[b + 1] - 1))
-    picks.update(int(x) for x in rng.choice(T, size=min(n, T), replace=False))
-    return np.array(sorted(picks))
+def check_output(dtype: str, got: np.ndarray, ref: np.ndarray, rows=None, what="", heads: int = 0):
+    """Assert got matches ref within the tolerances. With heads > 1 it also
+    asserts that the comparison discriminates on this data: unless the first
+    two heads' reference outputs are identical (a token that sees only its own
+    row, a zero scale), the reference with their columns exchanged must fail
+    the same bar (so a head-permuted result could not pass)."""
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    max_abs, rel = errors(got, ref)
+    assert max_abs <= MAX_ABS[dtype], f"{what}: max-abs {max_abs:.3e} > {MAX_ABS[dtype]}"
+    assert rel <= REL_FRO[dtype], f"{what}: relative Frobenius {rel:.3e} > {REL_FRO[dtype]}"
+    if heads > 1:
+        _, rel_swapped = errors(swap_heads(ref, heads), ref)
+        assert rel_swapped == 0.0 or rel_swapped > REL_FRO[dtype], \
+            f"{what}: a head-swapped output would pass ({rel_swapped:.3e})"
+    return max_abs, rel
+
+
+def swap_heads(out: np.ndarray, heads: int, a: int = 0, b: int = 1) -> np.ndarray:
+    """Copy of out [T, heads * v] with the columns of heads a and b exchanged."""
+    v = out.shape[1] // heads
+    o = out.copy()
+    o[:, a * v:(a + 1) * v], o[:, b * v:(b + 1) * v] = out[:, b * v:(b + 1) * v], out[:, a * v:(a + 1) * v]
+    return o
 
 
 def oracle(w: dict, tokens=None):

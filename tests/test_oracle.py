@@ -189,8 +189,10 @@ def _paged_from_contiguous(seqs_rows, new_counts, bs, rng, hs, spare=3):
     return cache.reshape(NB, bs, 1, hs), bt, np.array(slots, dtype=np.int32)
 
 
-def _dense_case(rng, *, pasts, news, H, hs, vhs, rd, ro, bs, window=-1, do_rotary=True):
-    """Build a workload plus its dense contiguous expectation via torch SDPA."""
+def _dense_case(rng, *, pasts, news, H, hs, vhs, rd, ro, bs, window=-1, do_rotary=True, has_scale=True):
+    """Build a workload plus its dense contiguous expectation via torch SDPA.
+    has_scale=False leaves the scale attribute absent and lets SDPA apply its
+    own default (1/sqrt of the query width)."""
     dt = "f16"
     P = max(p + n for p, n in zip(pasts, news))
     tables = _exact_tables(P, rd) if do_rotary else None
@@ -227,7 +229,7 @@ def _dense_case(rng, *, pasts, news, H, hs, vhs, rd, ro, bs, window=-1, do_rotar
             mask &= (qpos - kpos) <= window
         o = F.scaled_dot_product_attention(Q, K[None, None].expand(1, H, ctx, hs),
                                            K[None, None, :, :vhs].expand(1, H, ctx, vhs),
-                                           attn_mask=mask, scale=float(np.float32(0.125)))
+                                           attn_mask=mask, scale=float(np.float32(0.125)) if has_scale else None)
         expect.append(o[0].permute(1, 0, 2).reshape(n, H * vhs).numpy())
     cache, bt, slots = _paged_from_contiguous(
         [np.concatenate([r[:p], np.zeros((n, hs), np.uint16)]) for r, p, n in zip(seqs_rows, pasts, news)],
@@ -237,7 +239,8 @@ def _dense_case(rng, *, pasts, news, H, hs, vhs, rd, ro, bs, window=-1, do_rotar
     w = dict(dtype=dt, attrs=dict(num_heads=H, head_size=hs, v_head_size=vhs, block_size=bs,
                                   do_rotary=int(do_rotary), rotary_interleaved=0,
                                   rotary_dim=rd if do_rotary else 0, rotary_offset=ro if do_rotary else 0,
-                                  local_window_size=window, softcap=0.0, has_scale=1, scale=0.125),
+                                  local_window_size=window, softcap=0.0, has_scale=int(has_scale),
+                                  scale=0.125 if has_scale else 0.0),
              query=np.concatenate(queries).reshape(T, H * hs), key=np.concatenate(keys).reshape(T, hs),
              key_cache=cache, cos_cache=cos_bits, sin_cache=sin_bits,
              cumulative_sequence_length=cum, past_seqlens=np.array(pasts, np.int32),
@@ -259,6 +262,28 @@ def test_oracle_equals_dense_contiguous_attention(do_rotary, window):
     for b, rows in enumerate(seqs_rows):
         for j in range(len(rows)):
             assert np.array_equal(flat[bt[b, j // 16] * 16 + j % 16], rows[j])
+
+
+@pytest.mark.parametrize("hs,atol", [(64, 1e-10), (48, 1e-6)])
+def test_default_scale_equals_sdpa_default(hs, atol):
+    """No explicit scale and v_head_size == head_size: the op's default
+    1/sqrt(head_size) (docs.rs page, execute, scale rule) equals SDPA's own
+    default scale. With head_size 64 both are exactly 1/8; with 48 the op forms
+    the scale in float32, so the outputs agree to float32 rounding of the scale."""
+    rng = np.random.default_rng(60 + hs)
+    w, expect, _ = _dense_case(rng, pasts=[0, 21], news=[20, 5], H=3, hs=hs, vhs=hs, rd=16, ro=hs - 16,
+                               bs=16, has_scale=False)
+    assert orc.effective_scale(w["attrs"]) == float(np.float32(1.0) / np.sqrt(np.float32(hs)))
+    _, out = orc.run(w)
+    np.testing.assert_allclose(out, expect, rtol=0, atol=atol)
+
+
+def test_default_scale_absent_with_narrow_values_is_rejected():
+    a = dict(num_heads=1, head_size=64, v_head_size=32, has_scale=0, scale=0.0)
+    with pytest.raises(ValueError):
+        orc.effective_scale(a)
+    # v_head_size 0 means head_size: the default applies
+    assert orc.effective_scale(dict(a, v_head_size=0)) == 0.125
 
 
 def test_first_token_output_is_its_own_value_row():
