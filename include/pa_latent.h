@@ -196,6 +196,27 @@ pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_late
                                      void* output, void* workspace, size_t workspace_bytes,
                                      int32_t split_kv, void* stream);
 
+/*
+ * pa_latent_attention for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * read phase, with the same kernels and results, but its workspace is a
+ * static device array inside the library (64 MiB, one per device the library
+ * runs on, held until the process ends) instead of a caller buffer. The call
+ * itself allocates nothing. Arguments and errors are those of
+ * pa_latent_attention; a call whose workspace (pa_latent_workspace_size)
+ * exceeds 64 MiB returns PA_ERR_WORKSPACE_TOO_SMALL before any launch. Every
+ * call on one device shares that device's array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that overlap on one
+ * device (different streams, or threads without ordering) race and give
+ * undefined results.
+ */
+pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_latent_dims* dims,
+                                      pa_dtype dtype, const void* query, const void* key_cache,
+                                      const void* cos_cache, const void* sin_cache,
+                                      const int32_t* cumulative_sequence_length,
+                                      const int32_t* past_seqlens, const int32_t* block_table,
+                                      void* output, void* stream);
+
 /* Measurement hook (not part of the method). `before` and `after` are
  * hipEvent_t handles created by the caller, or NULL. The next
  * pa_latent_attention / pa_latent_attention_splits call made on this thread

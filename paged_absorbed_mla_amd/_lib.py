@@ -25,7 +25,8 @@ PA_F16 = 10
 PA_BF16 = 16
 
 EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention",
-            "pa_latent_attention_splits", "pa_latent_profile_next", "pa_last_error", "pa_latent_abi_version")
+            "pa_latent_attention_splits", "pa_latent_attention_noalloc", "pa_latent_profile_next", "pa_last_error",
+            "pa_latent_abi_version")
 
 
 class pa_latent_attrs(ctypes.Structure):
@@ -84,6 +85,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_latent_attention_splits.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                ctypes.c_int32, vp]
     lib.pa_latent_attention_splits.restype = ctypes.c_int
+    lib.pa_latent_attention_noalloc.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pa_latent_attention_noalloc.restype = ctypes.c_int
     lib.pa_latent_profile_next.argtypes = [vp, vp]
     lib.pa_latent_profile_next.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -171,6 +174,17 @@ def pa_latent_attention_splits(attrs, dims, dtype, query, key_cache, cos_cache, 
                                         _ptr(cumulative_sequence_length), _ptr(past_seqlens),
                                         _ptr(block_table), _ptr(output), _ptr(workspace), int(workspace_bytes),
                                         int(split_kv), _stream(stream, output, query))
+    return _check(st) if check else st
+
+
+def pa_latent_attention_noalloc(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache,
+                                cumulative_sequence_length, past_seqlens, block_table, output, stream=None,
+                                check=True):
+    lib = load()
+    st = lib.pa_latent_attention_noalloc(ctypes.byref(attrs), ctypes.byref(dims), int(dtype), _ptr(query),
+                                         _ptr(key_cache), _ptr(cos_cache), _ptr(sin_cache),
+                                         _ptr(cumulative_sequence_length), _ptr(past_seqlens), _ptr(block_table),
+                                         _ptr(output), _stream(stream, output, query))
     return _check(st) if check else st
 
 

@@ -17,7 +17,17 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+
+// Device scratch of pa_latent_attention_noalloc: the workspace that entry
+// point uses instead of a caller-provided one. Each device the library runs
+// on holds its own copy for the life of the process. In host code `scratch`
+// names a host-side stand-in, not the device array: its device address comes
+// from hipGetSymbolAddress, once per device (static_scratch below).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -163,6 +173,23 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   return PA_OK;
 }
 
+// Device address of `scratch` on the current device `dev`, looked up on the
+// first call on that device (with it current) and kept per device.
+pa_status static_scratch(int dev, void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) { *ptr = it->second; return PA_OK; }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return device_error(e, "hipGetSymbolAddress(scratch)");
+  if (!p) return fail(PA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+  addr[dev] = p;
+  *ptr = p;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +256,34 @@ pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_late
                                      void* workspace, size_t workspace_bytes, int32_t split_kv, void* stream) {
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, workspace, workspace_bytes, split_kv != 0, stream);
+}
+
+pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                                      const void* query, const void* key_cache, const void* cos_cache,
+                                      const void* sin_cache, const int32_t* cumulative_sequence_length,
+                                      const int32_t* past_seqlens, const int32_t* block_table, void* output,
+                                      void* stream) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_prof_ev[0] = g_prof_ev[1] = nullptr;
+    return device_error(e, "hipGetDevice");
+  }
+  void* ws = nullptr;
+  size_t need = 0;
+  pa_status st = static_scratch(dev, &ws);
+  if (st == PA_OK) st = pa_latent_workspace_size(attrs, dims, dtype, dev, &need);
+  if (st == PA_OK && need > kStaticScratchBytes)
+    st = fail(PA_ERR_WORKSPACE_TOO_SMALL,
+              "pa_latent_attention_noalloc: this call needs %zu bytes of scratch; the library's static scratch "
+              "holds %zu (use pa_latent_attention with a caller workspace)",
+              need, kStaticScratchBytes);
+  if (st != PA_OK) {
+    g_prof_ev[0] = g_prof_ev[1] = nullptr;   // the registration is consumed by this call
+    return st;
+  }
+  return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
+                        past_seqlens, block_table, output, ws, kStaticScratchBytes, true, stream);
 }
 
 pa_status pa_latent_profile_next(void* before, void* after) {
