@@ -70,17 +70,16 @@ struct AttnParams {
   const uint16_t* sin_t;
   const int32_t* bt;
   uint16_t* out;
-  const int32_t* header;    // [0] work units U, [1] query tiles M, [2] partial slots used
+  const int32_t* header;    // [0] work units U, [1] query tiles M
   const int32_t* wg_range;  // [grid + 1] unit range of each workgroup
   const int32_t* wg_tile;   // [grid] query tile holding each workgroup's first unit
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
-  const uint16_t* zero16;   // 16 zero bytes
   float* part_ml;           // [slots][rows][2]: running max (log2 domain), denominator
   void* part_o;             // partial outputs acc / l (element type PartT<DT>): slot s, row r at s * part_slot + r * part_row
   int64_t part_slot;        // elements between slots (padded: not a power of two)
   int part_row;             // elements between rows (VHSP + 16 bytes)
   const uint16_t* qfrag;    // [T * H][HSP]: RoPE'd query in fragment order (four-wave 576 kernel)
-  int64_t nblk;             // num_blocks: block ids are clamped into [0, nblk)
+  int nblk;                 // num_blocks (< 2^31 / block_size): block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H, hs, vhs, bs_log2, MB;
   int ro, rd, do_rotary, interleaved, window;
@@ -248,9 +247,7 @@ __device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
 
 // Block id clamped into [0, nblk): a block_table entry outside the cache (a
 // violated precondition) then reads some cache block instead of faulting.
-__device__ __forceinline__ int clamp_block(int blk, int64_t nblk) {
-  return (int)min(max((int64_t)blk, (int64_t)0), nblk - 1);
-}
+__device__ __forceinline__ int clamp_block(int blk, int nblk) { return min(max(blk, 0), nblk - 1); }
 
 __device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
   const int32_t* q = (const int32_t*)ptr;
@@ -471,16 +468,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;
 
-  // Query tile containing unit u: the last i with mt[i].unit0 <= u.
-  int i;
-  {
-    int lo = 0, hi_ = ld_uniform(p.header + 1) - 1;
-    while (lo < hi_) {
-      const int mid = (lo + hi_ + 1) >> 1;
-      if (ld_uniform(&p.mt[mid].unit0) <= u) lo = mid; else hi_ = mid - 1;
-    }
-    i = lo;
-  }
+  int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
+  const int i_first = i;
   const bool softcap_on = p.softcap > 0.0f;
   // Byte offset, within its cache block, of the 16-byte chunk each lane copies
   // in copy instruction `it` (tile-independent).
@@ -493,7 +482,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.hs + lc * 8) * 2;
   }
 
-  while (u < u_end) {
+  const int n_tiles = ld_uniform(p.header + 1);   // query tiles of the schedule
+  while (u < u_end && i < n_tiles) {
     const MTile t = ld_uniform_tile(p.mt + i);
     const int next0 = ld_uniform(&p.mt[i + 1].unit0);
     const int ua = u;
@@ -669,7 +659,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           }
         }
       } else {
-        const int64_t slot = (int64_t)t.part_base + (wr - t.w_first);
+        // The workgroup's first piece goes to slot wr, a later one to G + tile.
+        const int64_t slot = i == i_first ? (int64_t)wr : (int64_t)gridDim.x + i;
         if (hi == 0) {
           float* ml = p.part_ml + (slot * RW + rloc) * 2;
           ml[0] = st.m_run;
@@ -696,11 +687,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     u = ub;
     ++i;
   }
+
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Merge the partials of every query tile that several workgroups processed.
-// Piece i of a row holds its normalised output o_i = acc_i / l_i (bfloat16
+// Partial slot of piece q of a split query tile t (the workgroups w_first,
+// w_first + 1, ...): a workgroup stores its first piece in slot w and a later
+// piece (only ever piece 0 of its tile) in slot G + tile, which the schedule
+// records as the tile's part_base.
+__device__ __forceinline__ int64_t piece_slot(const MTile& t, int q) {
+  return q == 0 ? (int64_t)t.part_base : (int64_t)t.w_first + q;
+}
+
+// Merge the partials of every query tile that several workgroups processed
+// (piece q's partial at slot piece_slot(t, q)). Piece i of a row holds its normalised output o_i = acc_i / l_i (bfloat16
 // for bfloat16 outputs, else float32: PartF32), its running max m_i (log2
 // domain) and denominator l_i; with
 // M = max_i m_i and c_i = 2^(m_i - M) l_i, out = sum_i c_i o_i / sum_i c_i
@@ -736,10 +736,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     if (r >= t.nrows) continue;
     const int c0 = (threadIdx.x % TPR) * 8;                 // channel of group 0; group v at c0 + 8 TPR v
     if (c0 >= p.vhs) continue;
-    const float* ml = p.part_ml + ((int64_t)t.part_base * RW + r) * 2;   // piece q at + q * RW * 2
-    // Piece q's slice at element + q * part_slot (16-byte aligned: row and
-    // slot strides are multiples of 16 bytes).
-    const int64_t po0 = (int64_t)t.part_base * p.part_slot + (int64_t)r * p.part_row + c0;
+    // Piece q's (m, l) and slice (16-byte aligned: row and slot strides are
+    // multiples of 16 bytes).
+    auto ml_of = [&](int q) -> const float* { return p.part_ml + (piece_slot(t, q) * RW + r) * 2; };
+    auto po_of = [&](int q) -> int64_t { return piece_slot(t, q) * p.part_slot + (int64_t)r * p.part_row + c0; };
     float acc[NV][8];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
@@ -760,10 +760,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       for (int k = 0; k < QA; ++k) {
         const bool ok = k < nq;
         const int q = ok ? k : 0;
-        m[k] = ok ? ml[(int64_t)q * RW * 2] : -INFINITY;
-        l[k] = ok ? ml[(int64_t)q * RW * 2 + 1] : 0.0f;
+        m[k] = ok ? ml_of(q)[0] : -INFINITY;
+        l[k] = ok ? ml_of(q)[1] : 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po0 + (int64_t)q * p.part_slot + 8 * TPR * v, a[k][v]);
+        for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po_of(q) + 8 * TPR * v, a[k][v]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -785,8 +785,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 #pragma unroll
         for (int k = 0; k < QM; ++k) {
           const bool ok = q0 + k < nq;
-          m[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2] : -INFINITY;
-          l[k] = ok ? ml[(int64_t)(q0 + k) * RW * 2 + 1] : 0.0f;
+          m[k] = ok ? ml_of(q0 + k)[0] : -INFINITY;
+          l[k] = ok ? ml_of(q0 + k)[1] : 0.0f;
         }
         float bm = -INFINITY;
 #pragma unroll
@@ -807,8 +807,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
           const bool ok = q0 + k < nq;
           const int q = ok ? q0 + k : q0;
 #pragma unroll
-          for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po0 + (int64_t)q * p.part_slot + 8 * TPR * v, a[k][v]);
-          const float m = ml[(int64_t)q * RW * 2], l = ml[(int64_t)q * RW * 2 + 1];
+          for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po_of(q) + 8 * TPR * v, a[k][v]);
+          const float m = ml_of(q)[0], l = ml_of(q)[1];
           wq[k] = (!ok || m == -INFINITY) ? 0.0f : fast_exp2(m - mx) * l * inv;
         }
 #pragma unroll
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 }
 
 // Launches the attention kernel (events ev[0] / ev[1] recorded around it when
-// ev is non-null) and, when `combine`, the split-KV combine.
+// ev is non-null) and, when `combine`, the split-KV combine over `cgrid` query tiles.
 typedef hipError_t (*AttnLaunchFn)(const AttnParams&, int, bool, int, hipStream_t, const hipEvent_t*);
 typedef hipError_t (*AttnOccFn)(int*);
 

@@ -37,37 +37,36 @@ struct SchedParams {
   int32_t* wg_tile;
   int32_t* sched;    // global scratch for the arrays below when they exceed kSchedLdsInts
   MTile* mt;
-  uint32_t* zero16;
 };
 
 constexpr int kSchedThreads = 256;
 
-// Exclusive prefix sum over n values get(i), written with put(i, prefix);
-// returns the total. Every thread of the block must call it. Per chunk of
-// kSchedThreads values: a shuffle scan inside each wave, then every thread
-// adds the totals of the waves before its own (read from LDS in parallel, no
-// serial pass).
+// Exclusive prefix sum over n values get(i) (32-bit; every total here is an
+// index below 2^31), written with put(i, prefix); returns the total. Every
+// thread of the block must call it. Per chunk of kSchedThreads values: a
+// shuffle scan inside each wave, then every thread adds the totals of the
+// waves before its own (read from LDS in parallel, no serial pass).
 template <typename Get, typename Put>
-__device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
+__device__ int32_t block_exclusive_scan(int64_t n, Get get, Put put) {
   constexpr int NWV = kSchedThreads / 64;
-  __shared__ int64_t wave_sums[NWV];
+  __shared__ int32_t wave_sums[NWV];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t carry = 0;
+  int32_t carry = 0;
   for (int64_t base = 0; base < n; base += kSchedThreads) {
     const int64_t idx = base + threadIdx.x;
-    const int64_t v = idx < n ? get(idx) : 0;
-    int64_t x = v;
+    const int32_t v = idx < n ? get(idx) : 0;
+    int32_t x = v;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int64_t y = __shfl_up(x, d);
+      const int32_t y = __shfl_up(x, d);
       if (lane >= d) x += y;
     }
     if (lane == 63) wave_sums[wave] = x;
     __syncthreads();
-    int64_t before = 0, total = 0;
+    int32_t before = 0, total = 0;
 #pragma unroll
     for (int k = 0; k < NWV; ++k) {
-      const int64_t ws = wave_sums[k];
+      const int32_t ws = wave_sums[k];
       before += k < wave ? ws : 0;
       total += ws;
     }
@@ -78,47 +77,6 @@ __device__ int64_t block_exclusive_scan(int64_t n, Get get, Put put) {
   return carry;
 }
 
-// In-place inclusive prefix maximum of a[0, n) (LDS or global); every thread
-// of the block must call it.
-__device__ void block_inclusive_max_scan(int32_t* a, int64_t n) {
-  constexpr int NWV = kSchedThreads / 64;
-  __shared__ int32_t wave_max[NWV];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t carry = INT32_MIN;
-  for (int64_t base = 0; base < n; base += kSchedThreads) {
-    const int64_t idx = base + threadIdx.x;
-    int32_t x = idx < n ? a[idx] : INT32_MIN;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t y = __shfl_up(x, d);
-      if (lane >= d) x = max(x, y);
-    }
-    if (lane == 63) wave_max[wave] = x;
-    __syncthreads();
-    int32_t before = carry, total = carry;
-#pragma unroll
-    for (int k = 0; k < NWV; ++k) {
-      const int32_t wm = wave_max[k];
-      if (k < wave) before = max(before, wm);
-      total = max(total, wm);
-    }
-    if (idx < n) a[idx] = max(before, x);
-    carry = total;
-    __syncthreads();
-  }
-}
-
-// Workgroup w covers units [wg_range[w], wg_range[w+1]); the one that holds
-// unit u is the last w with wg_range[w] <= u.
-__device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int u) {
-  int lo = 0, hi = grid - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (wg_range[mid] <= u) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Blocks 1.. of the schedule launch: the query in the four-wave kernel's
 // fragment order, RoPE applied (float32 math, nearest-even rounding; the same
 // rotation the write phase applies to key rows). Each sequence's rows are cut
@@ -126,139 +84,208 @@ __device__ __forceinline__ int wg_of_unit(const int32_t* wg_range, int grid, int
 // and which has nv rows keeps the span [R0, R0 + nv) * hsp and stores 8-channel
 // chunk c of its row l (zero past hs) at chunk c * nv + l, so the wave reads
 // k-step s (chunks 2 s and 2 s + 1 of every row) as one contiguous run of
-// 32 nv bytes. Threads take chunks in destination order (coalesced stores).
-// `cum` and `pst` are cumulative_sequence_length and past_seqlens (staged in
-// LDS when they fit).
+// 32 nv bytes.
 //
-// Where chunk d of the fragment-ordered copy comes from: query row R and
-// channel c0 (the chunk's first), and the row's sequence b.
-// A chunk whose token the sequence bounds do not place inside [0, T) (only a
-// violated precondition does that) gets c0 = hsp: it is stored as zeros and
-// nothing is read for it.
-struct FragSrc {
-  int64_t R;
-  int c0, b;
+// The copy is a transpose through LDS, kPreRows consecutive query rows at a
+// time (whatever blocks they belong to): their contiguous bytes are loaded
+// with coalesced 16-byte loads into LDS rows padded to an odd number of
+// chunks, the rotary chunks are rotated there, and each chunk is stored to its
+// place by threads that take consecutive rows of one channel chunk, so the
+// stores of a block's rows are contiguous runs as well. `cum` and `pst` are
+// cumulative_sequence_length and past_seqlens (staged in LDS when they fit).
+// A row whose token the sequence bounds do not place inside [0, T) (only a
+// violated precondition does that) is not stored.
+constexpr int kPreRows = 32;
+constexpr int kSchedLdsBytes = 65536;
+constexpr int kPreMaxCpr = 72;                                       // chunks per row of a 576-wide copy
+constexpr int kPreItems = (kPreRows * kPreMaxCpr + kSchedThreads - 1) / kSchedThreads;   // chunks per thread
+constexpr int kPreTBytes = kPreRows * (kPreMaxCpr | 1) * 16;         // transpose buffer
+// Per-row placement, behind the transpose buffer: first destination chunk of
+// the row's column 0 (-1: not placed), its block's row count, position.
+struct PreRow {
+  int64_t dst0;
+  int32_t nv, pos;
 };
+constexpr int kPreRowBytes = kPreRows * (int)sizeof(PreRow);
 
-__device__ __forceinline__ FragSrc frag_source(const SchedParams& p, int64_t d, const int32_t* cum) {
-  const int cpr = p.hsp >> 3;                          // chunks per row
-  const int64_t Rg = d / cpr;                          // a row of the block holding chunk d
-  const int64_t tok = Rg / p.H;
-  FragSrc f;
-  f.b = find_seq(cum, p.B, tok);
-  const int64_t lo = cum[f.b], hi = cum[f.b + 1];
-  if (!(0 <= lo && lo <= tok && tok < hi && hi <= p.T)) {
-    f.R = 0;
-    f.c0 = p.hsp;
-    return f;
-  }
-  const int64_t s0 = lo * p.H;                         // the sequence's first row
-  const int64_t rows_b = (hi - lo) * p.H;
-  const int64_t k32 = (Rg - s0) & ~(int64_t)31;        // block's first row within the sequence
-  const int64_t R0 = s0 + k32;
-  const int nv = (int)min((int64_t)32, rows_b - k32);  // >= 1: Rg lies in the block
-  const int local = (int)(d - R0 * cpr);               // in [0, nv * cpr)
-  const int c = local / nv;
-  f.R = R0 + (local - c * nv);
-  f.c0 = c * 8;
-  return f;
-}
-
-// Chunks d0, d0 + stride, ... (KB of them, those below n) of the copy: the
-// plain loads of the batch go out together, then rotary chunks are rotated
-// and every chunk is stored.
-template <typename DT, int KB>
-__device__ __forceinline__ void query_frag_batch(const SchedParams& p, int64_t d0, int64_t stride, int64_t n,
-                                                 const int32_t* cum, const int32_t* pst) {
-  FragSrc f[KB];
-  u32x4_t v[KB];
+template <typename DT>
+__device__ void query_frag_rows(const SchedParams& p, int64_t R_base, uint8_t* lds, const int32_t* cum,
+                                const int32_t* pst) {
+  const int cpr = p.hsp >> 3;                          // chunks per row of the copy (<= kPreMaxCpr)
+  const int qcpr = p.hs >> 3;                          // chunks per query row
+  const int pitch = cpr | 1;                           // LDS row pitch in chunks (odd: conflict-free columns)
+  const int nr = (int)min((int64_t)kPreRows, p.T * p.H - R_base);
+  if (cpr > kPreMaxCpr) return;                        // only the 576-wide copy exists
+  PreRow* const rows = (PreRow*)(lds + kPreTBytes);
+  auto at = [&](int r, int c) -> u32x4_t* { return (u32x4_t*)(lds + (r * pitch + c) * 16); };
+  // All loads of the group in flight together (chunk k of the contiguous span).
+  const u32x4_t* src = (const u32x4_t*)(p.query + R_base * p.hs);
+  u32x4_t v[kPreItems];
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    const int64_t d = d0 + k * stride;
-    v[k] = u32x4_t{0u, 0u, 0u, 0u};
-    if (d < n) {
-      f[k] = frag_source(p, d, cum);
-      if (f[k].c0 < p.hs) v[k] = *(const u32x4_t*)(p.query + f[k].R * p.hs + f[k].c0);
+  for (int q = 0; q < kPreItems; ++q) {
+    const int k = q * kSchedThreads + threadIdx.x;
+    const int r = k / cpr, c = k - r * cpr;
+    v[q] = (r < nr && c < qcpr) ? src[r * qcpr + c] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // Meanwhile the rows' placement: block of 32 rows within the row's sequence.
+  if ((int)threadIdx.x < nr) {
+    const int64_t R = R_base + threadIdx.x;
+    const int64_t tok = R / p.H;
+    const int b = find_seq(cum, p.B, tok);
+    const int64_t lo = cum[b], hi = cum[b + 1];
+    PreRow pr;
+    pr.dst0 = -1;
+    pr.nv = 0;
+    pr.pos = 0;
+    if (0 <= lo && lo <= tok && tok < hi && hi <= p.T) {
+      const int64_t s0 = lo * p.H;                     // the sequence's first row
+      const int64_t k32 = (R - s0) & ~(int64_t)31;     // first row of R's block, within the sequence
+      const int64_t R0 = s0 + k32;
+      pr.nv = (int)min((int64_t)32, (hi - lo) * p.H - k32);
+      pr.dst0 = R0 * cpr + (R - R0);
+      pr.pos = (int)min(max((int64_t)pst[b] + (tok - lo), (int64_t)0), p.prow - 1);
     }
+    rows[threadIdx.x] = pr;
   }
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    const int64_t d = d0 + k * stride;
-    if (d >= n) continue;
-    const int c0 = f[k].c0;
-    if (p.rd > 0 && c0 >= p.ro && c0 < p.ro + p.rd && c0 < p.hs) {
-      const int b = f[k].b;
+  for (int q = 0; q < kPreItems; ++q) {
+    const int k = q * kSchedThreads + threadIdx.x;
+    const int r = k / cpr, c = k - r * cpr;
+    if (r < nr) *at(r, c) = v[q];
+  }
+  __syncthreads();
+  if (p.rd > 0) {
+    // Non-interleaved: one thread per (row, pair of chunks c, c + rd/16);
+    // interleaved: one per (row, rotary chunk), the pairs inside it.
+    const int half = p.rd >> 1;
+    const int per_row = p.interleaved ? p.rd >> 3 : p.rd >> 4;
+    for (int k = threadIdx.x; k < nr * per_row; k += kSchedThreads) {
+      const int r = k / per_row, j = k - r * per_row;
+      const PreRow pr = rows[r];
+      if (pr.dst0 < 0) continue;
+      const int c = (p.ro >> 3) + j;
       float x[8];
-      unpack8<DT>(v[k], x);
-      const int64_t t = f[k].R / p.H;
-      const int64_t pos = min(max((int64_t)pst[b] + (t - (int64_t)cum[b]), (int64_t)0), p.prow - 1);
-      rope_chunk<DT>(x, p.query + f[k].R * p.hs, c0, p.ro, p.rd, p.interleaved, pos, p.cos_t, p.sin_t);
-      v[k] = pack8<DT>(x);
+      unpack8<DT>(*at(r, c), x);
+      if (p.interleaved) {
+        const int64_t i0 = (int64_t)pr.pos * half + ((c * 8 - p.ro) >> 1);
+        const u32x2_t cv = *(const u32x2_t*)(p.cos_t + i0);
+        const u32x2_t sv = *(const u32x2_t*)(p.sin_t + i0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t cw = cv[e >> 1], sw = sv[e >> 1];
+          const float co = DT::to_f32((e & 1) ? (cw >> 16) : (cw & 0xFFFFu));
+          const float si = DT::to_f32((e & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+          const float xe = x[2 * e], xo = x[2 * e + 1];
+          x[2 * e] = xe * co - xo * si;
+          x[2 * e + 1] = xo * co + xe * si;
+        }
+        *at(r, c) = pack8<DT>(x);
+      } else {
+        const int cp = c + (half >> 3);                 // partner chunk, channel + rd/2
+        float xp[8], c8[8], s8[8];
+        unpack8<DT>(*at(r, cp), xp);
+        const int64_t i0 = (int64_t)pr.pos * half + (c * 8 - p.ro);
+        unpack8<DT>(*(const u32x4_t*)(p.cos_t + i0), c8);
+        unpack8<DT>(*(const u32x4_t*)(p.sin_t + i0), s8);
+        float y[8], yp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = x[e] * c8[e] - xp[e] * s8[e];
+          yp[e] = xp[e] * c8[e] + x[e] * s8[e];
+        }
+        *at(r, c) = pack8<DT>(y);
+        *at(r, cp) = pack8<DT>(yp);
+      }
     }
-    *(u32x4_t*)(p.qfrag + d * 8) = v[k];
+    __syncthreads();
   }
+  // Stores: consecutive threads take consecutive rows of one channel chunk.
+#pragma unroll
+  for (int q = 0; q < kPreItems; ++q) {
+    const int k = q * kSchedThreads + threadIdx.x;
+    if (k >= nr * cpr) continue;
+    const int c = k / nr, r = k - c * nr;
+    const PreRow pr = rows[r];
+    if (pr.dst0 < 0) continue;
+    *(u32x4_t*)(p.qfrag + (pr.dst0 + (int64_t)c * pr.nv) * 8) = *at(r, c);
+  }
+  __syncthreads();   // LDS free for the next rows
 }
 
-// Block 0 of the schedule launch builds the whole schedule in working arrays
-// and writes its outputs (tile table, workgroup ranges, header) only at the
-// end: a global store inside the build would make every later barrier wait
-// for its write to complete. The arrays live in LDS when they fit (then the
-// build runs on LDS instructions: IN_LDS is a template argument, so the
-// compiler sees the LDS array itself), else in the workspace.
-constexpr int kSchedLdsInts = 12288;
+// Block 0 of the schedule launch builds the schedule. Its working arrays
+// (per sequence: token range, past length, first query tile; per query tile:
+// sequence, rows, key range, first work unit) live in LDS when they fit
+// (IN_LDS is a template argument, so the compiler sees the LDS array), else
+// in the workspace. The outputs are written once, in the last phase, where no
+// barrier follows: a global store before a barrier would make the barrier
+// wait for it.
+//
+// Work units are the KV tiles of every query tile, laid end to end. With
+// split-KV on, each query tile is charged piece_units virtual units before
+// its first real one (the cost of the query load and the epilogue a piece
+// adds), and the virtual line of Uv = U + piece_units * M units is cut at
+// x(w) = floor(w Uv / G) for w = 0..G (x(w) = min(w, Uv) when Uv < G); a cut
+// inside a tile's virtual prefix falls on the tile's first unit. Because the
+// cuts have a closed form, every query tile finds the workgroups whose cuts
+// land in its range by counting, not searching: cnt(v), the number of cuts
+// below v, gives the first workgroup W_i of tile i's range, the number P_i of
+// cuts in its virtual prefix, and so the first workgroup that holds one of
+// its units (W_i + P_i - 1) and the last (W_{i+1} - 1).
+//
+// Partial slots (split tiles only): a workgroup stores the partial result of
+// its first piece in slot w and that of a later piece of query tile i in slot
+// G + i (only a workgroup's first and last pieces can be partial, and a tile
+// starts inside at most one workgroup's range), so at most G + M slots.
+constexpr int kSchedLdsInts = kSchedLdsBytes / 4;
 
-__host__ __device__ inline int64_t sched_ints(int B, int64_t max_mtiles, int grid) {
-  return 3 * (int64_t)B + 2 + 9 * max_mtiles + 1 + 2 * (int64_t)grid + 1;
+__host__ __device__ inline int64_t sched_ints(int B, int64_t max_mtiles, int /*grid*/) {
+  return 4 * (int64_t)B + 1 + 6 * max_mtiles + 1;
 }
 
 template <bool IN_LDS>
 __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* lds_arr) {
   int32_t* const base = IN_LDS ? lds_arr : p.sched;
-  int32_t* const cum = base;                           // [B + 1] cumulative_sequence_length
-  int32_t* const pst = cum + (p.B + 1);                // [B] past lengths (negative -> 0)
+  int32_t* const tlo = base;                           // [B] first token of each sequence
+  int32_t* const thi = tlo + p.B;                      // [B] end token
+  int32_t* const pst = thi + p.B;                      // [B] past length
   int32_t* const sbase = pst + p.B;                    // [B + 1] first query tile of each sequence
   int32_t* const u0 = sbase + (p.B + 1);               // [max_mtiles + 1] KV tiles, then first unit
-  int32_t* const np = u0 + (p.max_mtiles + 1);        // [max_mtiles] workgroups per query tile
-  int32_t* const tb = np + p.max_mtiles;               // [max_mtiles] sequence of each tile
-  int32_t* const trow = tb + p.max_mtiles;             // [max_mtiles] first row, then rows (2 x)
+  int32_t* const tb = u0 + (p.max_mtiles + 1);         // [max_mtiles] sequence of each tile
+  int32_t* const trow = tb + p.max_mtiles;             // [max_mtiles] first row, rows (2 x)
   int32_t* const tkv = trow + 2 * p.max_mtiles;        // [max_mtiles] kv_lo, kv_hi (2 x)
-  int32_t* const wr = tkv + 2 * p.max_mtiles;          // [grid + 1] unit range of every workgroup
-  int32_t* const wt = wr + (p.grid + 1);               // [grid] query tile of every workgroup
-  int32_t* const tw0 = wt + p.grid;                    // [max_mtiles] first workgroup of each tile
-  int32_t* const tw1 = tw0 + p.max_mtiles;             // [max_mtiles] last workgroup of each tile
 
-  // Sequence bounds and past lengths, forced into the ranges the
+  // A. Sequence bounds and past lengths, forced into the ranges the
   // preconditions promise (a violated precondition then gives unspecified
-  // values but no access outside the caller's buffers): bounds clamped into
-  // [0, T] and made non-decreasing, past lengths into [0, MB * bs].
-  for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
-    cum[b] = (int32_t)min(max((int64_t)p.cumseq[b], (int64_t)0), p.T);
-    if (b < p.B) pst[b] = min(max(p.past[b], 0), p.max_pos);
+  // values but no access outside the caller's buffers): token ranges clamped
+  // into [0, T] (empty when reversed), past lengths into [0, MB * bs].
+  for (int b = threadIdx.x; b < p.B; b += kSchedThreads) {
+    const int32_t lo = (int32_t)min(max((int64_t)p.cumseq[b], (int64_t)0), p.T);
+    const int32_t hi = (int32_t)min(max((int64_t)p.cumseq[b + 1], (int64_t)lo), p.T);
+    tlo[b] = lo;
+    thi[b] = hi;
+    pst[b] = min(max(p.past[b], 0), p.max_pos);
   }
   __syncthreads();
-  block_inclusive_max_scan(cum, p.B + 1);
-  // A. query tiles per sequence, prefix-summed into sbase.
+  // B. Query tiles per sequence, prefix-summed into sbase.
   const int64_t M_all = block_exclusive_scan(
       p.B,
-      [&](int64_t b) -> int64_t {
-        const int64_t rows = (int64_t)(cum[b + 1] - cum[b]) * p.H;
-        return (rows + p.RW - 1) / p.RW;
-      },
-      [&](int64_t b, int64_t v) { sbase[b] = (int32_t)v; });
-  // M cannot exceed max_mtiles when cumseq[B] = T (a precondition); clamp so a
-  // violated precondition cannot write past the tile table.
+      [&](int64_t b) -> int32_t { return (int32_t)(((int64_t)(thi[b] - tlo[b]) * p.H + p.RW - 1) / p.RW); },
+      [&](int64_t b, int32_t v) { sbase[b] = v; });
+  // At most max_mtiles: the clamped ranges hold at most T tokens in at most
+  // min(B, T) non-empty sequences.
   const int M = (int)min(M_all, p.max_mtiles);
   if (threadIdx.x == 0) sbase[p.B] = (int32_t)M_all;
   __syncthreads();
-  // B. describe every query tile; its KV tile count goes to u0 for now.
+  // C. Every query tile: its sequence (last b with sbase[b] <= i), rows, key
+  // range and KV tile count; then the count's prefix sum into u0.
   for (int i = threadIdx.x; i < M; i += kSchedThreads) {
-    int lo = 0, hi = p.B - 1;  // last b with sbase[b] <= i
+    int lo = 0, hi = p.B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (sbase[mid] <= i) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int rows = (cum[b + 1] - cum[b]) * p.H;
+    const int rows = (thi[b] - tlo[b]) * p.H;
     const int row0 = (i - sbase[b]) * p.RW;
     const int nrows = min(p.RW, rows - row0);
     const int pos0 = pst[b] + row0 / p.H;
@@ -273,90 +300,67 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     u0[i] = (kv_hi + p.KT - 1) / p.KT - kv_lo / p.KT;
   }
   __syncthreads();
-  // C. units: prefix sum of KV tiles.
   const int64_t U = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { return u0[i]; }, [&](int64_t i, int64_t v) { u0[i] = (int32_t)v; });
+      M, [&](int64_t i) -> int32_t { return u0[i]; }, [&](int64_t i, int32_t v) { u0[i] = v; });
   if (threadIdx.x == 0) u0[M] = (int32_t)U;
   __syncthreads();
-  // D. unit range of every workgroup. Split-KV: the units are laid out with
-  // piece_units virtual units before each query tile (the cost of the query
-  // load and epilogue a piece adds), and the virtual line is cut evenly; a
-  // workgroup that enters a second query tile thus takes fewer KV tiles. A
-  // cut inside a tile's virtual prefix falls on the tile's first unit.
-  // Empty ranges sit only at the end or right before a tile's first
-  // workgroup, so the workgroups that share a query tile are consecutive and
-  // each of them writes its partial slot.
-  const int64_t alpha = p.piece_units;
+
+  // D. Outputs: the tile table and the unit range and first tile of every
+  // workgroup.
+  const int G = p.grid;
+  const int64_t alpha = p.split_kv ? p.piece_units : 0;
   const int64_t Uv = U + alpha * M;
-  // Cut x(w) = floor(w Uv / grid) as w q + floor(w r / grid) with Uv = q grid
-  // + r: one 64-bit division per thread instead of one per workgroup
-  // (w r < grid^2 fits 32 bits for grids below 65536, the split launches'
-  // compute-unit multiples).
-  const int64_t vq = Uv / p.grid;
-  const uint32_t vr = (uint32_t)(Uv - vq * p.grid);
-  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
-    int32_t v;
-    if (!p.split_kv) {
-      v = u0[min(w, M)];
-    } else if (M == 0) {
-      v = 0;
-    } else {
-      const int64_t x = Uv < p.grid ? min((int64_t)w, Uv)
-                        : p.grid < 65536 ? (int64_t)w * vq + (int64_t)(((uint32_t)w * vr) / (uint32_t)p.grid)
-                                         : ((int64_t)w * Uv) / p.grid;
-      int lo = 0, hi = M - 1;   // last tile whose virtual start is <= x
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (u0[mid] + alpha * mid <= x) lo = mid; else hi = mid - 1;
-      }
-      const int64_t o = x - (u0[lo] + alpha * lo);
-      v = (int32_t)min(u0[lo] + max(o - alpha, (int64_t)0), (int64_t)u0[lo + 1]);
-    }
-    wr[w] = v;
-  }
-  __syncthreads();
-  // E. pieces per query tile, and the query tile holding each workgroup's
-  // first unit (the last i with u0[i] <= wr[w]).
+  // 32-bit divisions when every product below fits (the usual case).
+  const bool small = (Uv + alpha + 2) * (int64_t)G < ((int64_t)1 << 31);
+  auto cut = [&](int w) -> int64_t {                   // x(w)
+    if (Uv < G) return min((int64_t)w, Uv);
+    return small ? (int64_t)((uint32_t)w * (uint32_t)Uv / (uint32_t)G) : ((int64_t)w * Uv) / G;
+  };
+  auto cnt = [&](int64_t v) -> int {                   // cuts x(w), w in [0, G], below v
+    if (v <= 0) return 0;
+    if (Uv < G) return v <= Uv ? (int)v : G + 1;
+    const int64_t c = small ? (int64_t)(((uint32_t)v * (uint32_t)G + (uint32_t)Uv - 1) / (uint32_t)Uv)
+                            : (v * G + Uv - 1) / Uv;
+    return (int)min(c, (int64_t)G + 1);
+  };
   for (int i = threadIdx.x; i < M; i += kSchedThreads) {
-    const int w0 = wg_of_unit(wr, p.grid, u0[i]);
-    const int w1 = wg_of_unit(wr, p.grid, u0[i + 1] - 1);
-    np[i] = w1 - w0 + 1;
-    tw0[i] = w0;
-    tw1[i] = w1;
-  }
-  for (int w = threadIdx.x; w < p.grid; w += kSchedThreads) {
-    const int uw = wr[w];
-    int lo = 0, hi = M > 0 ? M - 1 : 0;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (u0[mid] <= uw) lo = mid; else hi = mid - 1;
-    }
-    wt[w] = lo;
-  }
-  __syncthreads();
-  // F. partial slots for the tiles that several workgroups share; np[i]
-  // becomes the tile's first slot (-1: one workgroup, no partial results).
-  const int64_t slots = block_exclusive_scan(
-      M, [&](int64_t i) -> int64_t { const int n = np[i]; return n > 1 ? n : 0; },
-      [&](int64_t i, int64_t v) { np[i] = np[i] > 1 ? (int32_t)v : -1; });
-  __syncthreads();
-  // Outputs, all stores at the end.
-  if (threadIdx.x < 4) p.zero16[threadIdx.x] = 0u;
-  for (int i = threadIdx.x; i < M; i += kSchedThreads) {
+    const int b = tb[i];
     MTile t;
-    t.b = tb[i];
+    t.b = b;
     t.row0 = trow[2 * i];
     t.nrows = trow[2 * i + 1];
     t.kv_lo = tkv[2 * i];
     t.kv_hi = tkv[2 * i + 1];
     t.unit0 = u0[i];
-    t.w_first = tw0[i];
-    t.npieces = tw1[i] - tw0[i] + 1;
-    t.part_base = np[i];
-    t.tok0 = cum[t.b];
-    t.past = pst[t.b];
+    t.tok0 = tlo[b];
+    t.past = pst[b];
     t.pad = 0;
+    if (p.split_kv) {
+      const int64_t Vi = u0[i] + alpha * i, Vn = u0[i + 1] + alpha * (i + 1);
+      const int Wi = cnt(Vi), Wn = cnt(Vn);
+      const int Pi = cnt(Vi + alpha + 1) - Wi;         // cuts inside the virtual prefix
+      t.w_first = Wi + Pi - 1;
+      t.npieces = Wn - t.w_first;
+      t.part_base = Pi > 0 ? t.w_first : G + i;        // slot of the first piece
+      for (int w = Wi; w < Wn; ++w) {
+        const int64_t o = cut(w) - Vi - alpha;
+        p.wg_range[w] = u0[i] + (int32_t)min(max(o, (int64_t)0), (int64_t)(u0[i + 1] - u0[i]));
+        p.wg_tile[w] = i;
+      }
+    } else {
+      t.w_first = i;
+      t.npieces = 1;
+      t.part_base = -1;
+      p.wg_range[i] = u0[i];
+      p.wg_tile[i] = i;
+    }
     p.mt[i] = t;
+  }
+  // Workgroups past the last cut inside a tile: empty ranges at the end.
+  const int wtail = p.split_kv ? (M > 0 ? cnt(Uv) : 0) : M;
+  for (int w = wtail + (int)threadIdx.x; w <= G; w += kSchedThreads) {
+    p.wg_range[w] = (int32_t)U;
+    if (w < G) p.wg_tile[w] = max(M - 1, 0);
   }
   if (threadIdx.x == 0) {
     MTile t = {};
@@ -364,43 +368,36 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     p.mt[M] = t;
     p.header[0] = (int32_t)U;
     p.header[1] = M;
-    p.header[2] = (int32_t)slots;
-  }
-  for (int w = threadIdx.x; w <= p.grid; w += kSchedThreads) {
-    p.wg_range[w] = wr[w];
-    if (w < p.grid) p.wg_tile[w] = wt[w];
   }
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
-  __shared__ int32_t lds_arr[kSchedLdsInts];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSchedLdsBytes];
   if (blockIdx.x > 0) {
-    // Token -> sequence search over LDS copies of the sequence bounds (one
-    // coalesced load per block instead of a chain of dependent global loads).
-    const bool staged = 2 * p.B + 1 <= kSchedLdsInts;
+    // Sequence bounds staged behind the transpose buffer when they fit (one
+    // coalesced load per block instead of chains of dependent global loads).
+    constexpr int kTBytes = kPreTBytes + kPreRowBytes;   // transpose buffer and row placements
+    static_assert(kPreTBytes % 16 == 0 && kTBytes < kSchedLdsBytes, "pre-pass LDS");
+    int32_t* const stage = (int32_t*)(lds + kTBytes);
+    const bool staged = 2 * (int64_t)p.B + 1 <= (kSchedLdsBytes - kTBytes) / 4;
     if (staged) {
       for (int b = threadIdx.x; b <= p.B; b += kSchedThreads) {
-        lds_arr[b] = p.cumseq[b];
-        if (b < p.B) lds_arr[p.B + 1 + b] = p.past[b];
+        stage[b] = p.cumseq[b];
+        if (b < p.B) stage[p.B + 1 + b] = p.past[b];
       }
       __syncthreads();
     }
-    const int32_t* cum = staged ? lds_arr : p.cumseq;
-    const int32_t* pst = staged ? lds_arr + p.B + 1 : p.past;
-    // Grid-stride over the chunks: the launch holds few of these blocks (the
-    // LDS array sized for block 0 allows three per CU), each thread taking a
-    // chunk per stride.
-    constexpr int KB = 4;   // chunks per thread whose loads are in flight together
-    const int64_t n = p.T * p.H * (p.hsp >> 3);
-    const int64_t stride = (int64_t)(gridDim.x - 1) * kSchedThreads;
-    for (int64_t idx = (int64_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x; idx < n; idx += KB * stride) {
-      if (p.dtype == 16) query_frag_batch<BF16, KB>(p, idx, stride, n, cum, pst);
-      else query_frag_batch<F16, KB>(p, idx, stride, n, cum, pst);
+    const int32_t* cum = staged ? stage : p.cumseq;
+    const int32_t* pst = staged ? stage + p.B + 1 : p.past;
+    const int64_t groups = (p.T * p.H + kPreRows - 1) / kPreRows;
+    for (int64_t gi = blockIdx.x - 1; gi < groups; gi += gridDim.x - 1) {
+      if (p.dtype == 16) query_frag_rows<BF16>(p, gi * kPreRows, lds, cum, pst);
+      else query_frag_rows<F16>(p, gi * kPreRows, lds, cum, pst);
     }
     return;
   }
-  if (sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts) schedule_build<true>(p, lds_arr);
-  else schedule_build<false>(p, lds_arr);
+  if (sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts) schedule_build<true>(p, (int32_t*)lds);
+  else schedule_build<false>(p, (int32_t*)lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -490,7 +487,6 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.part_cap = split_kv ? L.max_mtiles + L.ranges : 0;
   size_t off = 0;
   L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
-  L.off_zero = off; off = align256(off + 16);
   L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
   L.off_wg_tile = off; off = align256(off + (size_t)L.ranges * sizeof(int32_t));
   L.sched_ints = sched_ints(g.B, L.max_mtiles, L.ranges);
@@ -540,7 +536,6 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.sched = (int32_t*)(wsb + ws.off_sched);
   sp.piece_units = split_kv ? cfg.piece_units : 0;
   sp.mt = (MTile*)(wsb + ws.off_mtiles);
-  sp.zero16 = (uint32_t*)(wsb + ws.off_zero);
   sp.query = (const uint16_t*)query;
   sp.cos_t = (const uint16_t*)cos_t;
   sp.sin_t = (const uint16_t*)sin_t;
@@ -553,11 +548,11 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.rd = g.do_rotary ? g.rd : 0;   // 0: no rotary channels
   sp.interleaved = g.interleaved;
   sp.dtype = g.dtype;
-  // Query pre-pass blocks: at most kPrepassBlocks (two per compute unit of a
-  // 256-CU part; grid-stride loop).
+  // Query pre-pass blocks: one per kPreRows query rows, at most kPrepassBlocks
+  // (two per compute unit of a 256-CU part; grid-stride loop).
   constexpr int64_t kPrepassBlocks = 512;
-  const int64_t rope_chunks = sp.qfrag ? g.T * g.H * (cfg.hsp >> 3) : 0;
-  const int64_t rope_blocks = std::min<int64_t>((rope_chunks + kSchedThreads - 1) / kSchedThreads, kPrepassBlocks);
+  const int64_t rope_groups = sp.qfrag ? (g.T * g.H + kPreRows - 1) / kPreRows : 0;
+  const int64_t rope_blocks = std::min<int64_t>(rope_groups, kPrepassBlocks);
   schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -569,17 +564,16 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.sin_t = (const uint16_t*)sin_t;
   ap.bt = block_table;
   ap.out = (uint16_t*)out;
-  ap.header = sp.header;
   ap.wg_range = sp.wg_range;
   ap.wg_tile = sp.wg_tile;
   ap.mt = sp.mt;
-  ap.zero16 = (const uint16_t*)sp.zero16;
+  ap.header = sp.header;
   ap.part_ml = (float*)(wsb + ws.off_part_ml);
   ap.part_o = (void*)(wsb + ws.off_part_o);
   ap.part_slot = ws.part_slot;
   ap.part_row = ws.part_row;
   ap.qfrag = sp.qfrag;
-  ap.nblk = g.NB;
+  ap.nblk = (int)g.NB;   // NB * block_size <= INT32_MAX (checked by the entry points)
   ap.prow = g.do_rotary ? g.P : 1;
   ap.H = g.H;
   ap.hs = g.hs;

@@ -482,6 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;
   int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
+  const int i_first = i;
   const bool softcap_on = p.softcap > 0.0f;
 
   // Copy slot sl = it * 64 + lane of this wave is LDS row 8 w + sl / CPR,
@@ -498,7 +499,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     load_off[it] = lc * 8 < p.hs ? (uint32_t)((k * p.hs + lc * 8) * 2) : 0xFFFFu;
   }
 
-  while (u < u_end) {
+  const int n_tiles = ld_uniform(p.header + 1);   // query tiles of the schedule
+  while (u < u_end && i < n_tiles) {
     const MTile t = ld_uniform_tile(p.mt + i);
     const int next0 = ld_uniform(&p.mt[i + 1].unit0);
     const int ua = u;
@@ -779,7 +781,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int erloc = w * 32 + el32;
     const int etid = w * 64 + eln;
     if (ehi == 0) rowl[erloc] = l_tot;
-    const int64_t slot = whole ? 0 : (int64_t)t.part_base + (wr - t.w_first);
+    // Partial slot of a split piece: the workgroup's first piece goes to slot
+    // wr, a later one to G + tile.
+    const int64_t slot = whole ? 0 : (i == i_first ? (int64_t)wr : (int64_t)gridDim.x + i);
     if (!whole && ehi == 0 && erloc < t.nrows) {
       float* ml = p.part_ml + (slot * RW + erloc) * 2;
       ml[0] = st.m_ref;
@@ -879,6 +883,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     u = ub;
     ++i;
   }
+
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

@@ -45,7 +45,7 @@ struct WsLayout {
   int grid;             // workgroups of the attention launch
   int ranges;           // unit ranges of the schedule (one per workgroup)
   int64_t part_cap;     // partial-result slots
-  size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_zero, off_part_ml, off_part_o;
+  size_t off_header, off_wg_range, off_wg_tile, off_sched, off_mtiles, off_part_ml, off_part_o;
   int64_t sched_ints;   // scheduler scratch (int32) when it does not fit its LDS
   size_t off_qfrag;     // query in the four-wave kernel's fragment order, RoPE applied [T * H][hsp] (0: none)
   int64_t part_slot;    // partial-output elements between slots (bf16 or f32, by output type)
