@@ -11,11 +11,14 @@ values N(0,1)*0.5, scale 1/sqrt(192). Inputs are seeded synthetic data, resident
 in HBM before timing starts.
 
 Prints one JSON line. `value` is algorithmic TFLOP/s of the step (2 (hs+vhs)
-flops per (token, head, visible key)); `roofline` reports the dominant kernel
-(the attention kernel) against the HBM bound (this workload sits below the
-bf16 MFMA ridge): the phase's algorithmic bytes over the kernel's duration,
-measured live with HIP events that the library records around that launch on
-its stream, with the whole phase beside it;
+flops per (token, head, visible key)) over K back-to-back steps, by default
+captured into one HIP graph (`--launch eager` launches them from Python).
+`roofline` reports the dominant kernel (the attention kernel) against the HBM
+bound (this workload sits below the bf16 MFMA ridge): `frac` is the phase's
+algorithmic bytes over the kernel's mean duration, measured live with HIP
+events that the library records around that launch on its stream; beside it
+the same figures for the whole attention call (`phase`) and the whole step
+(`step`), mean/median/p10/p90, and per-step statistics after a MALL flush.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -48,6 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOADS))
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="graph: the timed steps are captured into one HIP graph and launched once; "
+                         "eager: launched one by one from Python")
+    ap.add_argument("--flush-steps", type=int, default=20,
+                    help="extra steps, each after a MALL flush, for per-step statistics (0: none)")
+    ap.add_argument("--flush-mib", type=int, default=512, help="scratch written before each flushed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -220,7 +229,99 @@ def cpu_baseline(w, target_s: float):
     dt = time.perf_counter() - t0
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"write phase for all {w['dims']['token_count']} tokens + attention for the first {b} "
-                      f"of {B} sequences ({done_tokens} tokens), {dt:.1f} s, float64 NumPy"}
+                      f"of {B} sequences ({done_tokens} tokens), {dt:.1f} s, float64 NumPy",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p10": round(float(np.percentile(a, 10)), 5), "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def timed_steps(torch, pa, dev, steps, graph):
+    """K back-to-back steps (write + attention) bracketed by events, with events
+    around each attention phase and, recorded by the library on its launch
+    stream, around each attention kernel. graph=True captures the K steps into
+    one HIP graph (after the eager warm-up, so every signature is warmed) and
+    times one launch of it."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a_, b_ in ev + kev:                 # torch creates an event on its first record
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+
+    def body(s):
+        # (inside a graph capture the events become graph nodes; only the
+        # bracketing events outside the graph are read then)
+        for k in range(steps):
+            dev.write()
+            ev[k][0].record(s)
+            pa.pa_latent_profile_next(kev[k][0], kev[k][1])
+            dev.attention()
+            ev[k][1].record(s)
+
+    start_all = torch.cuda.Event(enable_timing=True)
+    end_all = torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g.replay()                          # one untimed launch of the graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start_all.record(stream)
+        g.replay()
+        end_all.record(stream)
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        start_all.record(stream)
+        body(stream)
+        end_all.record(stream)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return (start_all.elapsed_time(end_all), [a.elapsed_time(b) for a, b in ev],
+            [a.elapsed_time(b) for a, b in kev], wall)
+
+
+def flushed_steps(torch, pa, dev, steps, mib):
+    """Steps with the 256 MB MALL (and the L2s) flushed before each: a write of
+    `mib` MiB of scratch outside the timed events, then one step with events
+    around the attention phase and its kernel. Per-step statistics."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(mib << 20, dtype=torch.uint8, device=dev.device)
+    phase, kern = [], []
+    for _ in range(steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ka.record(stream)
+        kb.record(stream)
+        dev.write()
+        a.record(stream)
+        pa.pa_latent_profile_next(ka, kb)
+        dev.attention()
+        b.record(stream)
+        torch.cuda.synchronize()
+        phase.append(a.elapsed_time(b))
+        kern.append(ka.elapsed_time(kb))
+    del scratch
+    return {"flush_mib": mib, "steps": steps, "phase_ms": stats(phase), "kernel_ms": stats(kern)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -250,42 +351,36 @@ def main():
     print(f"[bench] workload {args.config} generated in {time.perf_counter() - t_gen:.1f} s: "
           f"T={w['dims']['token_count']} B={w['dims']['batch']} kv_rows={counts['kv_rows']}", file=sys.stderr, flush=True)
     dev = DeviceWorkload(w, "cuda:0")
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         dev.step()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    # Events around the attention kernel itself, recorded by the library on its
-    # launch stream (pa_latent_profile_next); recorded once here so they exist.
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a_, b_ in kev:
-        a_.record(stream)
-        b_.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start_all = torch.cuda.Event(enable_timing=True)
-    end_all = torch.cuda.Event(enable_timing=True)
-    start_all.record(stream)
-    for k in range(args.steps):
-        dev.write()
-        ev[k][0].record(stream)
-        pa.pa_latent_profile_next(kev[k][0], kev[k][1])
-        dev.attention()
-        ev[k][1].record(stream)
-    end_all.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start_all.elapsed_time(end_all)
-    ms_step = ms_total / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    # K eager steps: events around every attention call and, recorded by the
+    # library on its launch stream, around every attention kernel (event
+    # timestamps recorded inside a HIP graph are not usable). Then, with
+    # --launch graph, the same K steps captured into one HIP graph and
+    # launched once: the whole-job time `value` is taken from that run.
+    ms_total_e, attn_ms, kern_ms, wall_e = timed_steps(torch, pa, dev, args.steps, False)
+    ms_step_e = ms_total_e / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
-    kern_ms = [a.elapsed_time(b) for a, b in kev]
     kern_avg_ms = float(np.mean(kern_ms))
-    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step; "
-          f"attention phase avg {attn_avg_ms:.4f} ms, median {np.median(attn_ms):.4f} ms; "
-          f"{attention_kernel_name(w)} avg {kern_avg_ms:.4f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps (eager): {ms_step_e:.4f} ms/step (events), wall "
+          f"{wall_e * 1e3 / args.steps:.4f} ms/step; attention phase avg {attn_avg_ms:.4f} ms, median "
+          f"{np.median(attn_ms):.4f} ms; {attention_kernel_name(w)} avg {kern_avg_ms:.4f} ms, median "
+          f"{np.median(kern_ms):.4f} ms", file=sys.stderr, flush=True)
+    ms_step, wall = ms_step_e, wall_e
+    if args.launch == "graph":
+        ms_total_g, _, _, wall = timed_steps(torch, pa, dev, args.steps, True)
+        ms_step = ms_total_g / args.steps
+        print(f"[bench] {args.steps} steps (one HIP graph): {ms_step:.4f} ms/step (events), wall "
+              f"{wall * 1e3 / args.steps:.4f} ms/step", file=sys.stderr, flush=True)
+    flushed = None
+    if args.flush_steps > 0:
+        flushed = flushed_steps(torch, pa, dev, args.flush_steps, args.flush_mib)
+        print(f"[bench] {args.flush_steps} steps after a {args.flush_mib} MiB MALL flush each: attention phase "
+              f"median {flushed['phase_ms']['median']:.4f} ms, kernel median {flushed['kernel_ms']['median']:.4f} ms",
+              file=sys.stderr, flush=True)
 
     flops = counts["flops"]
     byts = counts["bytes"]
@@ -303,17 +398,27 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(k_tflops / peak_tf, 4), "traffic": traffic}
-    phase_gbs = byts / (attn_avg_ms * 1e-3) / 1e9
-    phase_tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+    def side(ms):
+        gbs = byts / (ms * 1e-3) / 1e9
+        tfl = flops / (ms * 1e-3) / 1e12
+        return {"gbs": round(gbs, 1), "tflops": round(tfl, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(tfl / peak_tf, 4)}
     roof.update({
+        "frac_basis": f"{attention_kernel_name(w)}: algorithmic bytes (flops) of the attention phase over the "
+                      "kernel's mean duration, HIP events the library records around its launch on its stream",
         "kernel": f"{attention_kernel_name(w)} (HIP events on its launch stream)",
         "avg_ms": round(kern_avg_ms, 5),
+        "kernel_ms": stats(kern_ms),
         "alg_bytes_per_launch": int(byts), "alg_flops_per_launch": int(flops),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-        "phase": {"what": "pa_latent_attention: schedule + attention + combine", "avg_ms": round(attn_avg_ms, 5),
-                  "gbs": round(phase_gbs, 1), "tflops": round(phase_tflops, 1),
-                  "hbm_frac": round(phase_gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(phase_tflops / peak_tf, 4)},
+        "phase": dict({"what": "pa_latent_attention: schedule launch + attention kernel + combine (events around "
+                               "the call)", "avg_ms": round(attn_avg_ms, 5), "ms": stats(attn_ms)},
+                      **side(attn_avg_ms)),
+        "step": dict({"what": f"write + attention, whole-job time / steps ({args.launch} launch)",
+                      "ms": round(ms_step, 5), "eager_ms": round(ms_step_e, 5)}, **side(ms_step)),
     })
+    if flushed is not None:
+        roof["phase_after_mall_flush"] = dict(flushed, **side(flushed["phase_ms"]["median"]))
     out = {
         "metric": "paged-MLA decode attention TFLOP/s + HBM GB/s (% of roofline), 576/512 bf16",
         "value": round(tflops_step, 2),
@@ -327,6 +432,7 @@ def main():
         "vs_baseline": None,
         "dtype": w["dtype"],
         "data": "synthetic (seeded)",
+        "launch": args.launch,
         "config": {"workload": WORKLOADS[args.config], "tokens": w["dims"]["token_count"],
                    "batch": w["dims"]["batch"], "num_heads": w["attrs"]["num_heads"],
                    "head_size": w["attrs"]["head_size"], "v_head_size": w["attrs"]["v_head_size"],

@@ -25,6 +25,14 @@
  *     synchronise, read device memory back, or allocate memory; launch geometry
  *     depends only on `attrs` and `dims`, so the calls can be captured in a HIP
  *     graph once the workspace is allocated.
+ *   - Capture gate (docs.rs page, PagedCaptureSignature and capture_support;
+ *     PR #1978 "Invariants held", capture/replay safe): a call made while its
+ *     stream is being captured must have a warmed signature -- the same entry
+ *     point with the same dtype, attributes, dims and device has completed
+ *     once eagerly -- because the first eager call does the library's one-time
+ *     host work (occupancy query, code-object load). Otherwise it returns
+ *     PA_ERR_CAPTURE_NOT_WARMED and enqueues nothing. Replays of the captured
+ *     work compute exactly what the eager calls compute.
  *   - Every argument check runs before the first launch: on any error nothing
  *     is enqueued. Errors return a pa_status and set a thread-local message read
  *     by pa_last_error().
@@ -62,7 +70,8 @@ typedef enum {
   PA_ERR_INVALID_ARGUMENT = 1,    /* schema / geometry violation                      */
   PA_ERR_NOT_IMPLEMENTED = 2,     /* valid request outside what this build implements */
   PA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < pa_latent_workspace_size(...)  */
-  PA_ERR_DEVICE = 4               /* a HIP runtime call failed                        */
+  PA_ERR_DEVICE = 4,              /* a HIP runtime call failed                        */
+  PA_ERR_CAPTURE_NOT_WARMED = 5   /* stream capture of a signature not yet run eagerly */
 } pa_status;
 
 /* Storage type of the 16-bit tensors; values are the ONNX TensorProto codes. */
@@ -216,6 +225,16 @@ pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_lat
                                       const int32_t* cumulative_sequence_length,
                                       const int32_t* past_seqlens, const int32_t* block_table,
                                       void* output, void* stream);
+
+/*
+ * Capture readiness of a signature on `device` (docs.rs page,
+ * capture_support): *write_ready / *attention_ready are set to 1 when
+ * pa_latent_write / pa_latent_attention with these dtype, attrs and dims have
+ * completed eagerly on that device in this process (so they may be captured),
+ * else 0. Returns PA_OK, or PA_ERR_INVALID_ARGUMENT for NULL arguments.
+ */
+pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                                  int device, int32_t* write_ready, int32_t* attention_ready);
 
 /* Measurement hook (not part of the method). `before` and `after` are
  * hipEvent_t handles created by the caller, or NULL. The next

@@ -21,12 +21,13 @@ PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_NOT_IMPLEMENTED = 2
 PA_ERR_WORKSPACE_TOO_SMALL = 3
 PA_ERR_DEVICE = 4
+PA_ERR_CAPTURE_NOT_WARMED = 5
 PA_F16 = 10
 PA_BF16 = 16
 
 EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention",
-            "pa_latent_attention_splits", "pa_latent_attention_noalloc", "pa_latent_profile_next", "pa_last_error",
-            "pa_latent_abi_version")
+            "pa_latent_attention_splits", "pa_latent_attention_noalloc", "pa_latent_capture_ready",
+            "pa_latent_profile_next", "pa_last_error", "pa_latent_abi_version")
 
 
 class pa_latent_attrs(ctypes.Structure):
@@ -87,6 +88,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_latent_attention_splits.restype = ctypes.c_int
     lib.pa_latent_attention_noalloc.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.pa_latent_attention_noalloc.restype = ctypes.c_int
+    lib.pa_latent_capture_ready.argtypes = [A, D, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.pa_latent_capture_ready.restype = ctypes.c_int
     lib.pa_latent_profile_next.argtypes = [vp, vp]
     lib.pa_latent_profile_next.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -186,6 +190,14 @@ def pa_latent_attention_noalloc(attrs, dims, dtype, query, key_cache, cos_cache,
                                          _ptr(cumulative_sequence_length), _ptr(past_seqlens), _ptr(block_table),
                                          _ptr(output), _stream(stream, output, query))
     return _check(st) if check else st
+
+
+def pa_latent_capture_ready(attrs, dims, dtype, device=0):
+    """(write_ready, attention_ready) of this signature on `device`."""
+    w, a = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().pa_latent_capture_ready(ctypes.byref(attrs), ctypes.byref(dims), int(dtype), int(device),
+                                          ctypes.byref(w), ctypes.byref(a)))
+    return bool(w.value), bool(a.value)
 
 
 def pa_latent_profile_next(before, after):

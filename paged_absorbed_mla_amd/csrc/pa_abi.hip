@@ -17,9 +17,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 
 // Device scratch of pa_latent_attention_noalloc: the workspace that entry
 // point uses instead of a caller-provided one. Each device the library runs
@@ -127,13 +129,75 @@ pa_status device_error(hipError_t e, const char* what) {
   return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Warmed call signatures (docs.rs page, PagedCaptureSignature and the warm
+// gate in execute; PR #1978 "Invariants held": capture/replay safe after a
+// warmed call). A call made while its stream is being captured into a HIP
+// graph must have run eagerly before with the same signature on the same
+// device: the first eager call is where the library's one-time host work
+// happens (occupancy query, code-object load on the device, the static
+// scratch address), none of which may run inside a capture.
+enum Phase { kWrite = 0, kAttention = 1, kAttentionNoAlloc = 2 };
+
+struct Signature {
+  int32_t device, phase, dtype, split;
+  pa_latent_attrs a;
+  pa_latent_dims d;
+};
+
+Signature make_signature(int device, int phase, pa_dtype dtype, int split, const pa_latent_attrs* a,
+                         const pa_latent_dims* d) {
+  Signature s;
+  std::memset(&s, 0, sizeof(s));   // padding bytes take part in the comparison
+  s.device = device;
+  s.phase = phase;
+  s.dtype = (int32_t)dtype;
+  s.split = split;
+  std::memcpy(&s.a, a, sizeof(*a));
+  std::memcpy(&s.d, d, sizeof(*d));
+  return s;
+}
+
+std::mutex g_warm_mu;
+std::vector<Signature> g_warm;      // most recent last; bounded
+constexpr size_t kMaxWarm = 1024;
+
+bool is_warmed(const Signature& s) {
+  std::lock_guard<std::mutex> lk(g_warm_mu);
+  for (const auto& w : g_warm)
+    if (std::memcmp(&w, &s, sizeof(s)) == 0) return true;
+  return false;
+}
+
+void mark_warmed(const Signature& s) {
+  std::lock_guard<std::mutex> lk(g_warm_mu);
+  for (const auto& w : g_warm)
+    if (std::memcmp(&w, &s, sizeof(s)) == 0) return;
+  if (g_warm.size() >= kMaxWarm) g_warm.erase(g_warm.begin());
+  g_warm.push_back(s);
+}
+
+// Whether `stream` is being captured; a capture of an unwarmed signature is
+// rejected before anything is enqueued.
+pa_status capture_gate(void* stream, const Signature& s, bool* capturing) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+  if (e != hipSuccess) return device_error(e, "hipStreamIsCapturing");
+  *capturing = cs != hipStreamCaptureStatusNone;
+  if (*capturing && !is_warmed(s))
+    return fail(PA_ERR_CAPTURE_NOT_WARMED,
+                "stream capture of a call whose signature (dtype, attributes, shapes, device) has not run "
+                "eagerly: make the same call once outside the capture first");
+  return PA_OK;
+}
+
 // Events registered by pa_latent_profile_next for this thread's next attention call.
 thread_local hipEvent_t g_prof_ev[2] = {nullptr, nullptr};
 
 pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
                          const void* query, const void* key_cache, const void* cos_cache, const void* sin_cache,
                          const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* output,
-                         void* workspace, size_t workspace_bytes, bool split_kv, void* stream) {
+                         void* workspace, size_t workspace_bytes, bool split_kv, void* stream,
+                         int phase = kAttention) {
   hipEvent_t ev[2] = {g_prof_ev[0], g_prof_ev[1]};
   g_prof_ev[0] = g_prof_ev[1] = nullptr;
   const bool timed = ev[0] != nullptr && ev[1] != nullptr;
@@ -159,6 +223,9 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   int dev = 0, cus = 0, occ = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  const Signature sig = make_signature(dev, phase, dtype, split_kv ? 1 : 0, attrs, dims);
+  bool capturing = false;
+  if ((st = capture_gate(stream, sig, &capturing)) != PA_OK) return st;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return device_error(e, "hipDeviceGetAttribute");
   e = pa::attn_occupancy(g, cfg, dev, &occ);
@@ -169,6 +236,7 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   e = pa::launch_attention(g, cfg, ws, split_kv, query, key_cache, cos_cache, sin_cache, cumseq, past, block_table,
                            output, workspace, (hipStream_t)stream, timed ? ev : nullptr);
   if (e != hipSuccess) return device_error(e, "attention launch");
+  if (!capturing) mark_warmed(sig);
   g_last_error.clear();
   return PA_OK;
 }
@@ -210,9 +278,16 @@ pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* di
   if ((st = check_ptr(cos_cache, "cos_cache", any && g.do_rotary)) != PA_OK) return st;
   if ((st = check_ptr(sin_cache, "sin_cache", any && g.do_rotary)) != PA_OK) return st;
   if (!any) { g_last_error.clear(); return PA_OK; }
-  hipError_t e = pa::launch_write(g, key, cos_cache, sin_cache, slot_mapping, cumulative_sequence_length,
-                                  past_seqlens, key_cache, (hipStream_t)stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  const Signature sig = make_signature(dev, kWrite, dtype, 0, attrs, dims);
+  bool capturing = false;
+  if ((st = capture_gate(stream, sig, &capturing)) != PA_OK) return st;
+  e = pa::launch_write(g, key, cos_cache, sin_cache, slot_mapping, cumulative_sequence_length, past_seqlens,
+                       key_cache, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "write launch");
+  if (!capturing) mark_warmed(sig);
   g_last_error.clear();
   return PA_OK;
 }
@@ -271,7 +346,13 @@ pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_lat
   }
   void* ws = nullptr;
   size_t need = 0;
-  pa_status st = static_scratch(dev, &ws);
+  pa_status st = PA_OK;
+  if (attrs && dims && dims->token_count > 0) {
+    // The first call on a device looks up the scratch address: not inside a capture.
+    bool capturing = false;
+    st = capture_gate(stream, make_signature(dev, kAttentionNoAlloc, dtype, 1, attrs, dims), &capturing);
+  }
+  if (st == PA_OK) st = static_scratch(dev, &ws);
   if (st == PA_OK) st = pa_latent_workspace_size(attrs, dims, dtype, dev, &need);
   if (st == PA_OK && need > kStaticScratchBytes)
     st = fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -283,7 +364,17 @@ pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_lat
     return st;
   }
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
-                        past_seqlens, block_table, output, ws, kStaticScratchBytes, true, stream);
+                        past_seqlens, block_table, output, ws, kStaticScratchBytes, true, stream, kAttentionNoAlloc);
+}
+
+pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                                  int device, int32_t* write_ready, int32_t* attention_ready) {
+  if (!attrs || !dims || !write_ready || !attention_ready)
+    return fail(PA_ERR_INVALID_ARGUMENT, "NULL argument to pa_latent_capture_ready");
+  *write_ready = is_warmed(make_signature(device, kWrite, dtype, 0, attrs, dims)) ? 1 : 0;
+  *attention_ready = is_warmed(make_signature(device, kAttention, dtype, 1, attrs, dims)) ? 1 : 0;
+  g_last_error.clear();
+  return PA_OK;
 }
 
 pa_status pa_latent_profile_next(void* before, void* after) {
