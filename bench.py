@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="print the markdown summary of four rocprofv3 --pmc output directories: FETCH_SIZE "
                          "and WRITE_SIZE of the bench, then of --calibrate-copy")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print the markdown summary of rocprofv3 --pmc output directories (SQ/GRBM counters)")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
     return ap.parse_args()
 
@@ -191,6 +193,47 @@ def summarize_counters(fetch_d: str, write_d: str, cal_fetch_d: str, cal_write_d
         print("\nMachine-readable figures for `bench.py` (`sources` names the kernel sources these counters "
               "belong to; bench.py reports `traffic` only while they are unchanged):\n")
         print("```json\n" + json.dumps(blob) + "\n```")
+    if cmd:
+        print(f"\nCommands: {cmd}")
+
+
+def summarize_pmc(dirs, cmd: str):
+    """Per-kernel means of every counter in the given --pmc runs (one dispatch
+    per row of counter_collection.csv), with the kernel's mean duration from
+    the same runs' kernel traces, and derived MFMA figures: MFMA-busy SIMD
+    cycles (SQ_VALU_MFMA_BUSY_CYCLES) per SIMD over the kernel duration at the
+    2.4 GHz peak clock, and over the waves' lifetime (SQ_WAVE_CYCLES counts
+    quad-cycles; one wave per SIMD in the 576/512 kernel)."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
+    for d in dirs:
+        for r in _rocprof_rows(d, "counter_collection.csv"):
+            vals[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            durs[_short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    simds = 256 * 4
+    for k in sorted(vals):
+        if not k.startswith("pa::") and "pa::" not in k:
+            continue
+        c = {n: sum(v) / len(v) for n, v in vals[k].items()}
+        print(f"\n`{k}` (mean over {max(len(v) for v in vals[k].values())} dispatches per counter; "
+              f"duration {sum(durs[k]) / len(durs[k]):.1f} us mean)\n")
+        print("| counter | per dispatch |\n|---|---|")
+        for n in sorted(c):
+            print(f"| {n} | {c[n]:,.0f} |")
+        dur = sum(durs[k]) / len(durs[k])
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+            print(f"\n- MFMA-busy cycles per SIMD: {busy:,.0f} = {100 * busy / (dur * 2400):.1f}% of the "
+                  f"duration at the 2.4 GHz peak clock")
+            if "SQ_WAVE_CYCLES" in c:
+                life = 4 * c["SQ_WAVE_CYCLES"] / simds
+                print(f"- wave lifetime per SIMD {life:,.0f} cycles (SQ_WAVE_CYCLES x 4): MFMA busy "
+                      f"{100 * busy / life:.1f}% of it")
+        for mops in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"):
+            if mops in c:
+                print(f"- MFMA flops ({mops} x 512): {c[mops] * 512 / 1e9:,.1f} GFLOP per dispatch = "
+                      f"{c[mops] * 512 / (dur * 1e-6) / 1e12:,.0f} TFLOP/s over the dispatch")
     if cmd:
         print(f"\nCommands: {cmd}")
 
@@ -331,6 +374,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.cmd)
         return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
