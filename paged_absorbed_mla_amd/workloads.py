@@ -81,6 +81,8 @@ class Spec:
     spare_blocks: int = 8
     permute_blocks: bool = True
     seed: int = 0
+    layout: str = "LATENT"          # "LATENT" (one latent row per slot) or "SEPARATE" (GQA)
+    kv_num_heads: int = 1           # SEPARATE: key/value heads (num_heads is a multiple)
 
 
 # The five workloads. Sequence lengths that are drawn at random are drawn by
@@ -117,12 +119,36 @@ def _mixed(seed: int = 4) -> Spec:
                 local_window_size=1024, slot_drop_frac=0.05, seed=seed)
 
 
+# Grouped-query (SEPARATE layout) workloads: per-head key and value caches,
+# kv_num_heads key/value heads shared by groups of num_heads / kv_num_heads
+# query heads, full-width RoPE at offset 0. Llama-style 128-wide heads.
+def _gqa_tiny(seed: int = 5) -> Spec:
+    return Spec(name="gqa_tiny_64_64_32_prefill_decode", dtype="f16", past=[0, 21], new=[20, 16],
+                num_heads=4, head_size=64, v_head_size=64, rotary_dim=32, rotary_offset=0,
+                block_size=16, scale=0.0, has_scale=0, seed=seed, layout="SEPARATE", kv_num_heads=2)
+
+
+def _gqa_decode(seed: int = 6) -> Spec:
+    return Spec(name="gqa_128_decode", dtype="bf16", past=[], new=[],
+                num_heads=32, head_size=128, v_head_size=128, rotary_dim=128, rotary_offset=0,
+                block_size=16, scale=1.0 / math.sqrt(128.0), seed=seed, layout="SEPARATE", kv_num_heads=8)
+
+
+def _gqa_prefill(seed: int = 7) -> Spec:
+    return Spec(name="gqa_128_chunked_prefill", dtype="f16", past=[0, 512, 1024, 2048], new=[1024] * 4,
+                num_heads=32, head_size=128, v_head_size=128, rotary_dim=128, rotary_offset=0,
+                block_size=16, scale=1.0 / math.sqrt(128.0), seed=seed, layout="SEPARATE", kv_num_heads=8)
+
+
 CONFIGS = {
     "c1": _tiny,
     "c2": _glm_decode,
     "c3": _glm_prefill,
     "c4": _dsv3_decode,
     "c5": _mixed,
+    "gqa_tiny": _gqa_tiny,
+    "gqa_decode": _gqa_decode,
+    "gqa_prefill": _gqa_prefill,
 }
 
 
@@ -132,7 +158,7 @@ def draw_lengths(cfg: str, spec: Spec, rng: np.random.Generator, scale_down: int
     `scale_down` > 1 divides the drawn lengths and the sequence count, giving a
     smaller input with the same structure (used where the CPU oracle must
     finish in seconds)."""
-    if cfg == "c2":
+    if cfg in ("c2", "gqa_decode"):
         n = max(1, 32 // scale_down)
         spec.past = [int(x) for x in rng.integers(512 // scale_down, 4096 // scale_down, size=n, endpoint=True)]
         spec.new = [1] * n
@@ -147,7 +173,7 @@ def draw_lengths(cfg: str, spec: Spec, rng: np.random.Generator, scale_down: int
         dec = [int(x) for x in rng.integers(1024 // scale_down, 8192 // scale_down, size=ndec, endpoint=True)]
         spec.past = pre + dec
         spec.new = [max(1, 256 // scale_down)] * npre + [1] * ndec
-    elif cfg == "c3" and scale_down > 1:
+    elif cfg in ("c3", "gqa_prefill") and scale_down > 1:
         spec.past = [p // scale_down for p in spec.past]
         spec.new = [max(1, n // scale_down) for n in spec.new]
     elif cfg == "c1" and scale_down > 1:
@@ -187,15 +213,28 @@ def build(spec: Spec, cfg: Optional[str] = None, scale_down: int = 1, poison: bo
         block_table[b, :nblk] = phys[k:k + nblk]
         k += nblk
 
-    # Whole cache pre-filled, block by block, so memory stays bounded.
-    cache = np.empty((NB, bs, 1, hs), dtype=np.uint16)
-    chunk = max(1, (1 << 22) // (bs * hs))
-    for s in range(0, NB, chunk):
-        e = min(NB, s + chunk)
-        vals = rng.standard_normal((e - s, bs, 1, hs), dtype=np.float32) * np.float32(spec.cache_std)
-        cache[s:e] = to_storage_bits(vals, spec.dtype)
+    sep = spec.layout == "SEPARATE"
+    assert spec.layout in ("LATENT", "SEPARATE")
+    kvh = spec.kv_num_heads if sep else 1
+    vhs = spec.v_head_size or hs
+
+    def filled(width):
+        # Whole cache pre-filled, block by block, so memory stays bounded.
+        c = np.empty((NB, bs, kvh, width), dtype=np.uint16)
+        chunk = max(1, (1 << 22) // (bs * kvh * width))
+        for s in range(0, NB, chunk):
+            e = min(NB, s + chunk)
+            vals = rng.standard_normal((e - s, bs, kvh, width), dtype=np.float32) * np.float32(spec.cache_std)
+            c[s:e] = to_storage_bits(vals, spec.dtype)
+        return c
+
+    cache = filled(hs)
+    vcache = filled(vhs) if sep else None
     query = to_storage_bits(rng.standard_normal((T, H * hs), dtype=np.float32) * np.float32(spec.q_std), spec.dtype)
-    key = to_storage_bits(rng.standard_normal((T, hs), dtype=np.float32) * np.float32(spec.key_std), spec.dtype)
+    key = to_storage_bits(rng.standard_normal((T, kvh * hs), dtype=np.float32) * np.float32(spec.key_std),
+                          spec.dtype)
+    value = (to_storage_bits(rng.standard_normal((T, kvh * vhs), dtype=np.float32) * np.float32(spec.key_std),
+                             spec.dtype) if sep else None)
 
     cumseq = np.zeros(B + 1, dtype=np.int32)
     cumseq[1:] = np.cumsum(new)
@@ -228,8 +267,9 @@ def build(spec: Spec, cfg: Optional[str] = None, scale_down: int = 1, poison: bo
             rows = block_table[b, j // bs].astype(np.int64) * bs + j % bs
             reachable[rows] = True
         nan_bits = BF16_NAN_BITS if spec.dtype == "bf16" else F16_NAN_BITS
-        flat = cache.reshape(NB * bs, hs)
-        flat[~reachable] = nan_bits
+        for c in (cache, vcache):
+            if c is not None:
+                c.reshape(NB * bs, -1)[~reachable] = nan_bits
 
     attrs = dict(
         num_heads=H, head_size=hs, v_head_size=spec.v_head_size, block_size=bs,
@@ -239,12 +279,16 @@ def build(spec: Spec, cfg: Optional[str] = None, scale_down: int = 1, poison: bo
         has_scale=int(spec.has_scale), scale=float(spec.scale) if spec.has_scale else 0.0,
     )
     dims = dict(token_count=T, batch=B, max_blocks_per_seq=MB, num_blocks=NB, rotary_rows=P if rd > 0 else 0)
-    return dict(
+    out = dict(
         name=spec.name, dtype=spec.dtype, attrs=attrs, dims=dims,
         query=query, key=key, key_cache=cache, cos_cache=cos_bits, sin_cache=sin_bits,
         cumulative_sequence_length=cumseq, past_seqlens=past.astype(np.int32),
         block_table=block_table, slot_mapping=slot, spec=asdict(spec),
     )
+    if sep:
+        attrs.update(kv_cache_layout="SEPARATE", kv_num_heads=kvh)
+        out.update(value=value, value_cache=vcache)
+    return out
 
 
 def make(cfg: str, scale_down: int = 1, poison: bool = False, seed: Optional[int] = None) -> dict:
@@ -278,7 +322,12 @@ def algorithmic_counts(w: dict) -> dict:
             blocks += last // bs - first // bs + 1
     T = d["token_count"]
     esz = 2
-    byts = kv_rows * hs * esz + T * H * hs * esz + T * H * vhs * esz + T * a["rotary_dim"] * esz + blocks * 4
+    kvh = a.get("kv_num_heads", 1)
+    # LATENT: one latent row of hs channels per key (V is its leading part);
+    # SEPARATE: kv_num_heads key rows of hs and value rows of vhs channels.
+    row_bytes = (kvh * (hs + vhs) if a.get("kv_cache_layout") == "SEPARATE" else hs) * esz
+    new_row_bytes = row_bytes
+    byts = kv_rows * row_bytes + T * H * hs * esz + T * H * vhs * esz + T * a["rotary_dim"] * esz + blocks * 4
     flops = 2 * (hs + vhs) * H * pairs
     return dict(bytes=int(byts), flops=int(flops), kv_rows=int(kv_rows), visible_pairs=int(pairs) * H,
-                write_bytes=int(2 * T * hs * esz))
+                write_bytes=int(2 * T * new_row_bytes))
