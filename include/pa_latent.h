@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_LATENT_ABI_VERSION 1
+#define PA_LATENT_ABI_VERSION 2
 
 typedef enum {
   PA_OK = 0,
@@ -227,6 +227,61 @@ pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_lat
                                       void* output, void* stream);
 
 /*
+ * SEPARATE cache layout (grouped-query attention): the op's second dense mode,
+ * with a key cache and a separate value cache of kv_num_heads heads each
+ * (PR #1940 "PagedAttention v1 audit and MLA oracle", second commit: the
+ * oracle's SEPARATE mode -- GQA, RoPE, softcap, local window -- over the same
+ * block_table / slot_mapping addressing; third commit: num_heads must be a
+ * multiple of kv_num_heads; PR #1978 review "Gates verified": the schema's
+ * value and value_cache inputs). The pages print no kernel for it; where they
+ * are silent this library takes: query head h uses key/value head
+ * h / (num_heads / kv_num_heads) (consecutive heads form a group); RoPE, when
+ * on, rotates channels [rotary_offset, rotary_offset + rotary_dim) of every
+ * query head and every key head; value rows are stored unrotated; scale,
+ * softcap, window and the remaining attributes behave as in the latent layout.
+ * The attrs struct is the one above; kv_num_heads is passed beside it.
+ * Built for head_size <= 128 and v_head_size <= head_size, v_head_size a
+ * multiple of 8 (other valid sizes: PA_ERR_NOT_IMPLEMENTED).
+ *
+ * Write phase: for every token t with slot = slot_mapping[t] >= 0 and every
+ * key/value head g,
+ *   key_cache[slot, g]   = RN(RoPE(key[t, g*hs : (g+1)*hs], pos(t)))
+ *   value_cache[slot, g] = value[t, g*vhs : (g+1)*vhs]
+ *
+ *   key                        [T, kvH * hs]      dtype
+ *   value                      [T, kvH * vhs]     dtype
+ *   key_cache                  [NB, bs, kvH, hs]  dtype, updated in place
+ *   value_cache                [NB, bs, kvH, vhs] dtype, updated in place
+ *   other arguments as in pa_latent_write.
+ *
+ * Read phase: for token t and head h in group g,
+ *   q = RoPE(query[t, h*hs : (h+1)*hs], pos(t)); keys j as in pa_latent_attention;
+ *   s_j = scale * <q, key_cache[row_j, g]> (softcap applied when on);
+ *   output[t, h*vhs : (h+1)*vhs] = RN( sum_j softmax(s)_j * value_cache[row_j, g] )
+ * with query [T, H * hs], output [T, H * vhs], the workspace sized by
+ * pa_separate_workspace_size, and the other arguments as in
+ * pa_latent_attention. Errors, ordering, ownership, capture gate (the
+ * signature includes kv_num_heads) and trusted preconditions are those of the
+ * latent entry points; kv_num_heads < 1 or num_heads % kv_num_heads != 0 is
+ * PA_ERR_INVALID_ARGUMENT.
+ */
+pa_status pa_separate_write(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                            pa_dtype dtype, const void* key, const void* value, const void* cos_cache,
+                            const void* sin_cache, const int32_t* slot_mapping,
+                            const int32_t* cumulative_sequence_length, const int32_t* past_seqlens,
+                            void* key_cache, void* value_cache, void* stream);
+
+pa_status pa_separate_workspace_size(const pa_latent_attrs* attrs, int32_t kv_num_heads,
+                                     const pa_latent_dims* dims, pa_dtype dtype, int device, size_t* bytes);
+
+pa_status pa_separate_attention(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                                pa_dtype dtype, const void* query, const void* key_cache,
+                                const void* value_cache, const void* cos_cache, const void* sin_cache,
+                                const int32_t* cumulative_sequence_length, const int32_t* past_seqlens,
+                                const int32_t* block_table, void* output, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * Capture readiness of a signature on `device` (docs.rs page,
  * capture_support): *write_ready / *attention_ready are set to 1 when
  * pa_latent_write / pa_latent_attention with these dtype, attrs and dims have
@@ -238,7 +293,8 @@ pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_
 
 /* Measurement hook (not part of the method). `before` and `after` are
  * hipEvent_t handles created by the caller, or NULL. The next
- * pa_latent_attention / pa_latent_attention_splits call made on this thread
+ * pa_latent_attention / pa_latent_attention_splits / pa_separate_attention
+ * call made on this thread
  * records `before` on its stream immediately before the launch of its
  * attention kernel and `after` immediately after it, so hipEventElapsedTime
  * of the pair is that kernel's duration without the schedule and combine

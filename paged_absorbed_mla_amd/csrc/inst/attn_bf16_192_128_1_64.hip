@@ -2,4 +2,4 @@
 // query channels [0, 192) held in registers.
 #include "../pa_attn.cuh"
 
-PA_DEFINE_ATTN_INSTANCE(BF16, bf16, 192, 128, 1, 64, 192)
+PA_DEFINE_ATTN_INSTANCE(lat, BF16, bf16, 192, 128, 1, 64, 192)

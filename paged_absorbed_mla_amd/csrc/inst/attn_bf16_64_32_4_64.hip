@@ -2,4 +2,4 @@
 // query channels [0, 64) held in registers.
 #include "../pa_attn.cuh"
 
-PA_DEFINE_ATTN_INSTANCE(BF16, bf16, 64, 32, 4, 64, 64)
+PA_DEFINE_ATTN_INSTANCE(lat, BF16, bf16, 64, 32, 4, 64, 64)

@@ -2,4 +2,4 @@
 // query channels [0, 64) held in registers.
 #include "../pa_attn.cuh"
 
-PA_DEFINE_ATTN_INSTANCE(F16, f16, 64, 32, 1, 32, 64)
+PA_DEFINE_ATTN_INSTANCE(lat, F16, f16, 64, 32, 1, 32, 64)

@@ -9,8 +9,9 @@
 // "PagedAttention v1 audit and MLA oracle", third commit (rotary caches:
 // head_size % 16 == 0, rotary_dim = 2 * cos_cache.shape[1] with
 // cos_cache.shape[1] <= head_size / 2 and a multiple of 8); PR #1955 review
-// (rotary_offset % 8 == 0, head_size % 8 == 0). All checks run before any
-// launch.
+// (rotary_offset % 8 == 0, head_size % 8 == 0). The separate (grouped-query)
+// layout adds the head-ratio rule of PR #1940's third commit (num_heads a
+// multiple of kv_num_heads). All checks run before any launch.
 #include "../../include/pa_latent.h"
 #include "pa_internal.h"
 
@@ -47,17 +48,28 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-pa_status resolve(const pa_latent_attrs* a, const pa_latent_dims* d, pa_dtype dtype, pa::CallGeom* g) {
+// kv_num_heads: 0 for the latent layout (one latent head), else the key/value
+// heads of the separate layout.
+pa_status resolve(const pa_latent_attrs* a, const pa_latent_dims* d, pa_dtype dtype, pa::CallGeom* g,
+                  int kv_num_heads = 0) {
   if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "attrs is NULL");
   if (!d) return fail(PA_ERR_INVALID_ARGUMENT, "dims is NULL");
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype %d: only float16 (10) and bfloat16 (16) are implemented", (int)dtype);
   if (a->num_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_heads must be >= 1, got %d", a->num_heads);
+  const bool sep = kv_num_heads != 0;
+  if (sep && (kv_num_heads < 1 || a->num_heads % kv_num_heads != 0))
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads (%d) must be a multiple of kv_num_heads (%d)", a->num_heads,
+                kv_num_heads);
   if (a->head_size < 8 || a->head_size % 8 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "head_size must be a positive multiple of 8, got %d", a->head_size);
   const int hs = a->head_size;
   const int vhs = a->v_head_size == 0 ? hs : a->v_head_size;
-  if (vhs < 1 || vhs > hs)
+  if (vhs < 1) return fail(PA_ERR_INVALID_ARGUMENT, "v_head_size %d must be in 1..=head_size %d", vhs, hs);
+  if (sep && (vhs > hs || vhs % 8 != 0))
+    return fail(PA_ERR_NOT_IMPLEMENTED, "separate layout: v_head_size %d must be a multiple of 8 and <= head_size %d",
+                vhs, hs);
+  if (vhs > hs)
     return fail(PA_ERR_INVALID_ARGUMENT, "v_head_size %d must be in 1..=head_size %d", vhs, hs);
   const int bs = a->block_size;
   if (bs < 16 || (bs & (bs - 1)) != 0)
@@ -95,6 +107,10 @@ pa_status resolve(const pa_latent_attrs* a, const pa_latent_dims* d, pa_dtype dt
     return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq * block_size exceeds the position range");
   if (d->num_blocks * (int64_t)bs > (int64_t)INT32_MAX)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks * block_size exceeds the int32 slot range");
+  if (sep && (int64_t)d->batch * kv_num_heads > (int64_t)INT32_MAX / 8)
+    return fail(PA_ERR_INVALID_ARGUMENT, "batch * kv_num_heads exceeds the schedule's range");
+  if (sep && d->num_blocks * (int64_t)bs * kv_num_heads * hs > (int64_t)INT32_MAX * 64)
+    return fail(PA_ERR_INVALID_ARGUMENT, "key cache exceeds the addressable range");
   g->dtype = (int)dtype;
   g->H = a->num_heads;
   g->hs = hs;
@@ -115,6 +131,8 @@ pa_status resolve(const pa_latent_attrs* a, const pa_latent_dims* d, pa_dtype dt
   g->MB = d->max_blocks_per_seq;
   g->NB = d->num_blocks;
   g->P = d->rotary_rows;
+  g->sep = sep ? 1 : 0;
+  g->kvh = sep ? kv_num_heads : 1;
   return PA_OK;
 }
 
@@ -139,19 +157,20 @@ pa_status device_error(hipError_t e, const char* what) {
 enum Phase { kWrite = 0, kAttention = 1, kAttentionNoAlloc = 2 };
 
 struct Signature {
-  int32_t device, phase, dtype, split;
+  int32_t device, phase, dtype, split, kvh;
   pa_latent_attrs a;
   pa_latent_dims d;
 };
 
 Signature make_signature(int device, int phase, pa_dtype dtype, int split, const pa_latent_attrs* a,
-                         const pa_latent_dims* d) {
+                         const pa_latent_dims* d, int kvh = 0) {
   Signature s;
   std::memset(&s, 0, sizeof(s));   // padding bytes take part in the comparison
   s.device = device;
   s.phase = phase;
   s.dtype = (int32_t)dtype;
   s.split = split;
+  s.kvh = kvh;
   std::memcpy(&s.a, a, sizeof(*a));
   std::memcpy(&s.d, d, sizeof(*d));
   return s;
@@ -197,16 +216,17 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
                          const void* query, const void* key_cache, const void* cos_cache, const void* sin_cache,
                          const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* output,
                          void* workspace, size_t workspace_bytes, bool split_kv, void* stream,
-                         int phase = kAttention) {
+                         int phase = kAttention, int kvh = 0, const void* value_cache = nullptr) {
   hipEvent_t ev[2] = {g_prof_ev[0], g_prof_ev[1]};
   g_prof_ev[0] = g_prof_ev[1] = nullptr;
   const bool timed = ev[0] != nullptr && ev[1] != nullptr;
   pa::CallGeom g;
-  pa_status st = resolve(attrs, dims, dtype, &g);
+  pa_status st = resolve(attrs, dims, dtype, &g, kvh);
   if (st != PA_OK) return st;
   const bool any = g.T > 0;
   if ((st = check_ptr(query, "query", any)) != PA_OK) return st;
   if ((st = check_ptr(key_cache, "key_cache", any)) != PA_OK) return st;
+  if ((st = check_ptr(value_cache, "value_cache", any && g.sep)) != PA_OK) return st;
   if ((st = check_ptr(cumseq, "cumulative_sequence_length", any)) != PA_OK) return st;
   if ((st = check_ptr(past, "past_seqlens", any)) != PA_OK) return st;
   if ((st = check_ptr(block_table, "block_table", any)) != PA_OK) return st;
@@ -215,15 +235,15 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   if ((st = check_ptr(sin_cache, "sin_cache", any && g.do_rotary)) != PA_OK) return st;
   pa::AttnConfig cfg;
   if (!pa::choose_config(g, &cfg))
-    return fail(PA_ERR_NOT_IMPLEMENTED, "no attention instance for head_size %d / v_head_size %d (built: <= 576 / <= 512)",
-                g.hs, g.vhs);
+    return fail(PA_ERR_NOT_IMPLEMENTED, "no attention instance for head_size %d / v_head_size %d (built: %s)", g.hs,
+                g.vhs, g.sep ? "separate layout <= 128 / <= 128" : "<= 576 / <= 512");
   if (!any) { g_last_error.clear(); return PA_OK; }
   if (!workspace) return fail(PA_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0) return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   int dev = 0, cus = 0, occ = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_error(e, "hipGetDevice");
-  const Signature sig = make_signature(dev, phase, dtype, split_kv ? 1 : 0, attrs, dims);
+  const Signature sig = make_signature(dev, phase, dtype, split_kv ? 1 : 0, attrs, dims, kvh);
   bool capturing = false;
   if ((st = capture_gate(stream, sig, &capturing)) != PA_OK) return st;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -233,8 +253,8 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   const pa::WsLayout ws = pa::plan_workspace(g, cfg, cus, occ, split_kv);
   if (workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes, ws.total);
-  e = pa::launch_attention(g, cfg, ws, split_kv, query, key_cache, cos_cache, sin_cache, cumseq, past, block_table,
-                           output, workspace, (hipStream_t)stream, timed ? ev : nullptr);
+  e = pa::launch_attention(g, cfg, ws, split_kv, query, key_cache, value_cache, cos_cache, sin_cache, cumseq, past,
+                           block_table, output, workspace, (hipStream_t)stream, timed ? ev : nullptr);
   if (e != hipSuccess) return device_error(e, "attention launch");
   if (!capturing) mark_warmed(sig);
   g_last_error.clear();
@@ -258,46 +278,44 @@ pa_status static_scratch(int dev, void** ptr) {
   return PA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
-                          const void* key, const void* cos_cache, const void* sin_cache,
-                          const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
-                          const int32_t* past_seqlens, void* key_cache, void* stream) {
+pa_status write_impl(const pa_latent_attrs* attrs, int kvh, const pa_latent_dims* dims, pa_dtype dtype,
+                     const void* key, const void* value, const void* cos_cache, const void* sin_cache,
+                     const int32_t* slot_mapping, const int32_t* cumseq, const int32_t* past, void* key_cache,
+                     void* value_cache, void* stream) {
   pa::CallGeom g;
-  pa_status st = resolve(attrs, dims, dtype, &g);
+  pa_status st = resolve(attrs, dims, dtype, &g, kvh);
   if (st != PA_OK) return st;
   const bool any = g.T > 0;
   if ((st = check_ptr(key, "key", any)) != PA_OK) return st;
+  if ((st = check_ptr(value, "value", any && g.sep)) != PA_OK) return st;
   if ((st = check_ptr(slot_mapping, "slot_mapping", any)) != PA_OK) return st;
-  if ((st = check_ptr(cumulative_sequence_length, "cumulative_sequence_length", any)) != PA_OK) return st;
-  if ((st = check_ptr(past_seqlens, "past_seqlens", any)) != PA_OK) return st;
+  if ((st = check_ptr(cumseq, "cumulative_sequence_length", any)) != PA_OK) return st;
+  if ((st = check_ptr(past, "past_seqlens", any)) != PA_OK) return st;
   if ((st = check_ptr(key_cache, "key_cache", any)) != PA_OK) return st;
+  if ((st = check_ptr(value_cache, "value_cache", any && g.sep)) != PA_OK) return st;
   if ((st = check_ptr(cos_cache, "cos_cache", any && g.do_rotary)) != PA_OK) return st;
   if ((st = check_ptr(sin_cache, "sin_cache", any && g.do_rotary)) != PA_OK) return st;
   if (!any) { g_last_error.clear(); return PA_OK; }
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_error(e, "hipGetDevice");
-  const Signature sig = make_signature(dev, kWrite, dtype, 0, attrs, dims);
+  const Signature sig = make_signature(dev, kWrite, dtype, 0, attrs, dims, kvh);
   bool capturing = false;
   if ((st = capture_gate(stream, sig, &capturing)) != PA_OK) return st;
-  e = pa::launch_write(g, key, cos_cache, sin_cache, slot_mapping, cumulative_sequence_length, past_seqlens,
-                       key_cache, (hipStream_t)stream);
+  e = pa::launch_write(g, key, value, cos_cache, sin_cache, slot_mapping, cumseq, past, key_cache, value_cache,
+                       (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "write launch");
   if (!capturing) mark_warmed(sig);
   g_last_error.clear();
   return PA_OK;
 }
 
-pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
-                                   int device, size_t* bytes) {
+pa_status workspace_impl(const pa_latent_attrs* attrs, int kvh, const pa_latent_dims* dims, pa_dtype dtype,
+                         int device, size_t* bytes) {
   if (!bytes) return fail(PA_ERR_INVALID_ARGUMENT, "bytes is NULL");
   *bytes = 0;
   pa::CallGeom g;
-  pa_status st = resolve(attrs, dims, dtype, &g);
+  pa_status st = resolve(attrs, dims, dtype, &g, kvh);
   if (st != PA_OK) return st;
   pa::AttnConfig cfg;
   if (!pa::choose_config(g, &cfg))
@@ -313,6 +331,23 @@ pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent
   *bytes = a.total > b.total ? a.total : b.total;
   g_last_error.clear();
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_latent_write(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                          const void* key, const void* cos_cache, const void* sin_cache,
+                          const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
+                          const int32_t* past_seqlens, void* key_cache, void* stream) {
+  return write_impl(attrs, 0, dims, dtype, key, nullptr, cos_cache, sin_cache, slot_mapping,
+                    cumulative_sequence_length, past_seqlens, key_cache, nullptr, stream);
+}
+
+pa_status pa_latent_workspace_size(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                                   int device, size_t* bytes) {
+  return workspace_impl(attrs, 0, dims, dtype, device, bytes);
 }
 
 pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
@@ -365,6 +400,38 @@ pa_status pa_latent_attention_noalloc(const pa_latent_attrs* attrs, const pa_lat
   }
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, ws, kStaticScratchBytes, true, stream, kAttentionNoAlloc);
+}
+
+pa_status pa_separate_write(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                            pa_dtype dtype, const void* key, const void* value, const void* cos_cache,
+                            const void* sin_cache, const int32_t* slot_mapping,
+                            const int32_t* cumulative_sequence_length, const int32_t* past_seqlens, void* key_cache,
+                            void* value_cache, void* stream) {
+  if (kv_num_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "kv_num_heads must be >= 1, got %d", kv_num_heads);
+  return write_impl(attrs, kv_num_heads, dims, dtype, key, value, cos_cache, sin_cache, slot_mapping,
+                    cumulative_sequence_length, past_seqlens, key_cache, value_cache, stream);
+}
+
+pa_status pa_separate_workspace_size(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                                     pa_dtype dtype, int device, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (kv_num_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "kv_num_heads must be >= 1, got %d", kv_num_heads);
+  return workspace_impl(attrs, kv_num_heads, dims, dtype, device, bytes);
+}
+
+pa_status pa_separate_attention(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                                pa_dtype dtype, const void* query, const void* key_cache, const void* value_cache,
+                                const void* cos_cache, const void* sin_cache,
+                                const int32_t* cumulative_sequence_length, const int32_t* past_seqlens,
+                                const int32_t* block_table, void* output, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (kv_num_heads < 1) {
+    g_prof_ev[0] = g_prof_ev[1] = nullptr;
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_num_heads must be >= 1, got %d", kv_num_heads);
+  }
+  return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
+                        past_seqlens, block_table, output, workspace, workspace_bytes, true, stream, kAttention,
+                        kv_num_heads, value_cache);
 }
 
 pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,

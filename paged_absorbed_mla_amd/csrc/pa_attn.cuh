@@ -50,7 +50,11 @@
 
 namespace pa {
 
-// One query tile: rows [row0, row0 + nrows) of sequence b.
+// One query tile: rows [row0, row0 + nrows) of sequence b. A row is
+// token * H + head within the sequence, H the query heads that share one
+// key/value head (all of them in the latent layout). In the separate
+// (grouped-query) layout each sequence is scheduled once per key/value head
+// kvg, whose query heads are kvg * H .. kvg * H + H - 1.
 struct MTile {
   int32_t b, row0, nrows, kv_lo, kv_hi;
   int32_t unit0;      // first global work unit (one unit = one KV tile)
@@ -59,7 +63,7 @@ struct MTile {
   int32_t npieces;    // workgroups that process the tile
   int32_t tok0;       // first token of sequence b (cumulative_sequence_length, clamped into [0, T])
   int32_t past;       // past length of sequence b (clamped into [0, max_blocks_per_seq * block_size])
-  int32_t pad;
+  int32_t kvg;        // key/value head of the tile (0 in the latent layout)
 };
 static_assert(sizeof(MTile) == 48, "MTile layout");
 
@@ -79,9 +83,13 @@ struct AttnParams {
   int64_t part_slot;        // elements between slots (padded: not a power of two)
   int part_row;             // elements between rows (VHSP + 16 bytes)
   const uint16_t* qfrag;    // [T * H][HSP]: RoPE'd query in fragment order (four-wave 576 kernel)
+  const uint16_t* vcache;   // separate layout: value cache [slots][kvh][vhs] (null in the latent layout)
   int nblk;                 // num_blocks (< 2^31 / block_size): block ids are clamped into [0, nblk)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
-  int H, hs, vhs, bs_log2, MB;
+  int H;                    // query heads per key/value head (rows per token of a query tile)
+  int Hq;                   // query heads of the call (H * kvh): head stride of query and output rows
+  int krs, vrs;             // elements between cache slots: key cache (kvh * hs), value cache (kvh * vhs)
+  int hs, vhs, bs_log2, MB;
   int ro, rd, do_rotary, interleaved, window;
   float scale, scale_log2, softcap, softcap_inv;
 };
@@ -263,8 +271,14 @@ __device__ __forceinline__ MTile ld_uniform_tile(const MTile* ptr) {
   t.npieces = ld_uniform(q + 8);
   t.tok0 = ld_uniform(q + 9);
   t.past = ld_uniform(q + 10);
-  t.pad = 0;
+  t.kvg = ld_uniform(q + 11);
   return t;
+}
+
+// Query / output row of row R (token * H + head) of a tile's sequence.
+__device__ __forceinline__ int64_t head_row(const AttnParams& p, const MTile& t, int R) {
+  const int tq = R / p.H;
+  return (int64_t)(t.tok0 + tq) * p.Hq + t.kvg * p.H + (R - tq * p.H);
 }
 
 // State one wavefront carries across the KV tiles of a piece: its 32 query
@@ -278,11 +292,13 @@ struct WaveState {
   float m_run, l_run;
 };
 
-// S^T = K Q^T for one LDS tile, softmax update, O^T += V^T P^T.
-template <typename DT, int HSP, int VHSP, int KT, int QREG>
+// S^T = K Q^T for one LDS tile, softmax update, O^T += V^T P^T. K rows are
+// at L (CPR chunks each), V rows at LV (VCPR chunks each; LV = L when V is
+// the leading part of the latent row).
+template <typename DT, int HSP, int VHSP, int KT, int QREG, int VCPR>
 __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>& st, const uint8_t* L,
-                                             const uint16_t* qrest, int key0, int pos, int lo_row,
-                                             bool softcap_on, const AttnParams& p) {
+                                             const uint8_t* LV, const uint16_t* qrest, int key0, int pos,
+                                             int lo_row, bool softcap_on, const AttnParams& p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;
   constexpr int NKK = HSP / 16;
@@ -403,14 +419,14 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   const uint8_t* vb[2][2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
-    vb[0][par] = L + k0b * CPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
-    vb[1][par] = L + (k0b + 8) * CPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
+    vb[0][par] = LV + k0b * VCPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
+    vb[1][par] = LV + (k0b + 8) * VCPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
   }
   constexpr int VPF = 3;
   constexpr int VSTEPS = NSUB * 2 * NMT;
   auto pv_frag = [&](int n) -> u32x4_t {
     const int step = n / NMT, mt = n % NMT;        // step = sub * 2 + k2
-    const int coff = step * 16 * CPR * 16 + (mt >> 1) * 128;
+    const int coff = step * 16 * VCPR * 16 + (mt >> 1) * 128;
     const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[0][mt & 1] + coff));
     const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb[1][mt & 1] + coff));
     const u32x2_t d0 = __builtin_bit_cast(u32x2_t, r0);
@@ -431,25 +447,32 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG>
+// SEP: separate (grouped-query) layout -- K rows from the key cache, V rows
+// from the value cache into a second part of each LDS buffer; otherwise V is
+// the leading VHSP channels of the latent row already in the buffer.
+template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG, bool SEP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void attn_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;          // 16-byte chunks per LDS row
+  constexpr int VCPR = SEP ? VHSP / 8 : CPR;
   constexpr int TILE_CHUNKS = KT * CPR;
+  constexpr int VTILE_CHUNKS = SEP ? KT * VCPR : 0;
   constexpr int NT = NW * 64;
   constexpr int LOADS = TILE_CHUNKS / NT;
+  constexpr int VLOADS = VTILE_CHUNKS / NT;
   constexpr int NKK = HSP / 16;
   constexpr int NMT = VHSP / 32;
   constexpr int RW = NW * 32;
   constexpr int NBLK = KT / 16;         // most blocks a tile can touch (block_size >= 16)
   static_assert(HSP % 64 == 0 && VHSP % 32 == 0 && VHSP <= HSP, "head sizes");
-  static_assert(KT % 32 == 0 && TILE_CHUNKS % NT == 0, "tile shape");
+  static_assert(KT % 32 == 0 && TILE_CHUNKS % NT == 0 && VTILE_CHUNKS % NT == 0, "tile shape");
+  static_assert(!SEP || VHSP % 64 == 0, "value rows: whole swizzle periods");
   static_assert(QREG % 16 == 0 && QREG <= HSP, "register part of the query");
   // LDS: [KV tile buffers | persistent query rows, channels >= QREG]. Before the
   // tile loop the buffer region stages the register part of the query.
   constexpr int QSTRIDE = QREG + 8;     // staged rows padded by 16 bytes against bank conflicts
   constexpr int QRS = HSP - QREG + 8;
-  constexpr int BUF_BYTES = TILE_CHUNKS * 16;
+  constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
   constexpr int KV_BYTES = (2 * BUF_BYTES > QSTAGE_BYTES) ? 2 * BUF_BYTES : QSTAGE_BYTES;
   constexpr int QREST_BYTES = (QREG < HSP) ? RW * QRS * 2 : 0;
@@ -479,7 +502,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     const int pidx = it * NT + (int)threadIdx.x;
     const int k = pidx / CPR;
     const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-    load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.hs + lc * 8) * 2;
+    load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.krs + lc * 8) * 2;
+  }
+  int vload_off[VLOADS > 0 ? VLOADS : 1];
+#pragma unroll
+  for (int it = 0; it < VLOADS; ++it) {
+    const int pidx = it * NT + (int)threadIdx.x;
+    const int k = pidx / VCPR;
+    const int lc = (pidx - k * VCPR) ^ lds_swizzle(k);
+    vload_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.vrs + lc * 8) * 2;
   }
 
   const int n_tiles = ld_uniform(p.header + 1);   // query tiles of the schedule
@@ -492,18 +523,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     const int tile_b = tile_a + (ub - ua);
     const bool whole = (ua == t.unit0) && (ub == next0);
     const int b = t.b;
-    const int cum_b = t.tok0;
     const int past_b = t.past;
 
     const int rloc = w * 32 + l32;
     const bool row_ok = rloc < t.nrows;
     const int R = t.row0 + rloc;
     const int tq = R / p.H;
-    const int h = R - tq * p.H;
     const int pos = row_ok ? past_b + tq : -1;
     const int lo_row = p.window >= 0 ? max(0, pos - p.window) : 0;
     const bool wave_active = w * 32 < t.nrows;
-    const int64_t qrow = (int64_t)(cum_b + tq) * p.H + h;
+    const int64_t qrow = head_row(p, t, R);
 
     WaveState<DT, HSP, VHSP, KT, QREG> st;
     // Query rows of this wave, staged through LDS (free between pieces),
@@ -521,9 +550,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         const int rl = w * 32 + r;
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (rl < t.nrows && c0 < p.hs) {
-          const int Rr = t.row0 + rl;
-          const int tr = Rr / p.H;
-          const int64_t gq = (int64_t)(cum_b + tr) * p.H + (Rr - tr * p.H);
+          const int64_t gq = head_row(p, t, t.row0 + rl);
           v = *(const u32x4_t*)(p.query + gq * p.hs + c0);
         }
         *(u32x4_t*)qel(r, c0) = v;
@@ -575,7 +602,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 #pragma unroll
       for (int e = 0; e < NBLK; ++e) blks[e] = clamp_block(ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1)), p.nblk);
       uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
-      if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP) {
+      uint8_t* vdst0 = dst0 + TILE_CHUNKS * 16;
+      if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP && (!SEP || p.vhs == VHSP)) {
         // Interior tile: every slot is a real cache chunk.
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
@@ -583,8 +611,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           int blk = blks[0];
 #pragma unroll
           for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
-          const uint8_t* base = (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.hs);
+          const uint8_t* base =
+              (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.krs + t.kvg * p.hs);
           __builtin_amdgcn_global_load_lds(base + load_off[it], dst0 + it * NT * 16, 16, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < VLOADS; ++it) {
+          const int e = (((it * NW + w) * 64) / VCPR) >> p.bs_log2;
+          int blk = blks[0];
+#pragma unroll
+          for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
+          const uint8_t* base =
+              (const uint8_t*)(p.vcache + (((int64_t)blk << p.bs_log2) + in_blk) * p.vrs + t.kvg * p.vhs);
+          __builtin_amdgcn_global_load_lds(base + vload_off[it], vdst0 + it * NT * 16, 16, 0, 0);
         }
       } else {
         // Boundary tile: keys outside [kv_lo, kv_hi) or channels >= hs are zero-filled.
@@ -598,7 +637,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
           if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs) {
             const int blkv = clamp_block(p.bt[(int64_t)b * p.MB + min(j >> p.bs_log2, p.MB - 1)], p.nblk);
             const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
-            __builtin_amdgcn_global_load_lds(p.cache + row * p.hs + lc * 8, dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(p.cache + row * p.krs + t.kvg * p.hs + lc * 8, dst, 16, 0, 0);
+          } else {
+            *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll 1
+        for (int it = 0; it < VLOADS; ++it) {
+          const int pidx = it * NT + (int)threadIdx.x;
+          const int k = pidx / VCPR;
+          const int lc = (pidx - k * VCPR) ^ lds_swizzle(k);
+          const int j = key0 + k;
+          uint8_t* dst = vdst0 + it * NT * 16;
+          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.vhs) {
+            const int blkv = clamp_block(p.bt[(int64_t)b * p.MB + min(j >> p.bs_log2, p.MB - 1)], p.nblk);
+            const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
+            __builtin_amdgcn_global_load_lds(p.vcache + row * p.vrs + t.kvg * p.vhs + lc * 8, dst, 16, 0, 0);
           } else {
             *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
           }
@@ -613,8 +667,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
-        tile_compute<DT, HSP, VHSP, KT, QREG>(st, lds_raw + bufi * BUF_BYTES, qrest, tt * KT, pos, lo_row,
-                                              softcap_on, p);
+        const uint8_t* buf = lds_raw + bufi * BUF_BYTES;
+        tile_compute<DT, HSP, VHSP, KT, QREG, VCPR>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
+                                                    pos, lo_row, softcap_on, p);
       }
     } else {
       for (int tt = tile_a; tt < tile_b; ++tt) {
@@ -730,7 +785,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int r0 = blockIdx.y * kCombineRows;
   if (r0 >= t.nrows) return;
   const int nq = t.npieces;
-  const int cum_b = t.tok0;
   for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
     const int r = r0 + rr;
     if (r >= t.nrows) continue;
@@ -815,7 +869,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
         for (int k = 0; k < QA; ++k) add(wq[k], a[k]);
       }
     }
-    uint16_t* orow = p.out + ((int64_t)cum_b * p.H + t.row0 + r) * p.vhs + c0;
+    uint16_t* orow = p.out + head_row(p, t, t.row0 + r) * p.vhs + c0;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = c0 + 8 * TPR * v;
@@ -837,26 +891,30 @@ typedef hipError_t (*AttnOccFn)(int*);
 
 }  // namespace pa
 
-#define PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, SUF) attn_##DTN##_##HSP##_##VHSP##_##NW##_##KT##_##SUF
-#define PA_DEFINE_ATTN_INSTANCE(DT, DTN, HSP, VHSP, NW, KT, QREG)                                          \
-  namespace pa {                                                                                        \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                          \
-    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG>;                                  \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0); \
-  }                                                                                                     \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,     \
-                                                        int cgrid, hipStream_t s, const hipEvent_t* ev) { \
-    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                          \
-    if (e != hipSuccess) return e;                                                                      \
-    attn_kernel<DT, HSP, VHSP, NW, KT, QREG><<<grid, NW * 64, 0, s>>>(p);                               \
-    e = hipGetLastError();                                                                              \
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                            \
-    if (e != hipSuccess || !combine) return e;                                                          \
-    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);         \
-    return hipGetLastError();                                                                           \
-  }                                                                                                     \
+// Instance names: LAY is lat (V = leading part of the latent row) or sep (separate
+// value cache, grouped-query heads).
+#define PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, SUF) attn_##LAY##_##DTN##_##HSP##_##VHSP##_##NW##_##KT##_##SUF
+#define PA_SEP_lat false
+#define PA_SEP_sep true
+#define PA_DEFINE_ATTN_INSTANCE(LAY, DT, DTN, HSP, VHSP, NW, KT, QREG)                                      \
+  namespace pa {                                                                                          \
+  hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                       \
+    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY>;                      \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0);   \
+  }                                                                                                       \
+  hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,  \
+                                                             int cgrid, hipStream_t s, const hipEvent_t* ev) { \
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                            \
+    if (e != hipSuccess) return e;                                                                        \
+    attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY><<<grid, NW * 64, 0, s>>>(p);                   \
+    e = hipGetLastError();                                                                                \
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                              \
+    if (e != hipSuccess || !combine) return e;                                                            \
+    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);           \
+    return hipGetLastError();                                                                             \
+  }                                                                                                       \
   }
-#define PA_DECLARE_ATTN_INSTANCE(DTN, HSP, VHSP, NW, KT)                                                    \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch)(const AttnParams&, int, bool, int, hipStream_t,     \
-                                                       const hipEvent_t*);                                  \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)(int*);
+#define PA_DECLARE_ATTN_INSTANCE(LAY, DTN, HSP, VHSP, NW, KT)                                                   \
+  hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, launch)(const AttnParams&, int, bool, int, hipStream_t,    \
+                                                            const hipEvent_t*);                                 \
+  hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, occ)(int*);

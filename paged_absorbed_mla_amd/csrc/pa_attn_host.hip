@@ -20,6 +20,7 @@ struct SchedParams {
   const int32_t* cumseq;
   const int32_t* past;
   int B, H, RW, KT, window, grid, split_kv;
+  int kvh;           // key/value heads: each sequence is scheduled once per head (H = query heads per head)
   int max_pos;       // max_blocks_per_seq * block_size: past lengths are clamped to it
   int piece_units;   // virtual KV tiles charged at the start of every query tile
   // Query pre-pass (blocks 1.., four-wave 576 kernel): the query with RoPE
@@ -244,12 +245,15 @@ __host__ __device__ inline int64_t sched_ints(int B, int64_t max_mtiles, int /*g
 
 template <bool IN_LDS>
 __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* lds_arr) {
+  // Scheduled sequences: (sequence b, key/value head g) as sb = b * kvh + g;
+  // in the latent layout kvh = 1 and sb = b.
+  const int SB = p.B * p.kvh;
   int32_t* const base = IN_LDS ? lds_arr : p.sched;
-  int32_t* const tlo = base;                           // [B] first token of each sequence
-  int32_t* const thi = tlo + p.B;                      // [B] end token
-  int32_t* const pst = thi + p.B;                      // [B] past length
-  int32_t* const sbase = pst + p.B;                    // [B + 1] first query tile of each sequence
-  int32_t* const u0 = sbase + (p.B + 1);               // [max_mtiles + 1] KV tiles, then first unit
+  int32_t* const tlo = base;                           // [SB] first token of each sequence
+  int32_t* const thi = tlo + SB;                       // [SB] end token
+  int32_t* const pst = thi + SB;                       // [SB] past length
+  int32_t* const sbase = pst + SB;                     // [SB + 1] first query tile of each sequence
+  int32_t* const u0 = sbase + (SB + 1);                // [max_mtiles + 1] KV tiles, then first unit
   int32_t* const tb = u0 + (p.max_mtiles + 1);         // [max_mtiles] sequence of each tile
   int32_t* const trow = tb + p.max_mtiles;             // [max_mtiles] first row, rows (2 x)
   int32_t* const tkv = trow + 2 * p.max_mtiles;        // [max_mtiles] kv_lo, kv_hi (2 x)
@@ -258,28 +262,29 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   // preconditions promise (a violated precondition then gives unspecified
   // values but no access outside the caller's buffers): token ranges clamped
   // into [0, T] (empty when reversed), past lengths into [0, MB * bs].
-  for (int b = threadIdx.x; b < p.B; b += kSchedThreads) {
+  for (int sb = threadIdx.x; sb < SB; sb += kSchedThreads) {
+    const int b = sb / p.kvh;
     const int32_t lo = (int32_t)min(max((int64_t)p.cumseq[b], (int64_t)0), p.T);
     const int32_t hi = (int32_t)min(max((int64_t)p.cumseq[b + 1], (int64_t)lo), p.T);
-    tlo[b] = lo;
-    thi[b] = hi;
-    pst[b] = min(max(p.past[b], 0), p.max_pos);
+    tlo[sb] = lo;
+    thi[sb] = hi;
+    pst[sb] = min(max(p.past[b], 0), p.max_pos);
   }
   __syncthreads();
   // B. Query tiles per sequence, prefix-summed into sbase.
   const int64_t M_all = block_exclusive_scan(
-      p.B,
+      SB,
       [&](int64_t b) -> int32_t { return (int32_t)(((int64_t)(thi[b] - tlo[b]) * p.H + p.RW - 1) / p.RW); },
       [&](int64_t b, int32_t v) { sbase[b] = v; });
   // At most max_mtiles: the clamped ranges hold at most T tokens in at most
-  // min(B, T) non-empty sequences.
+  // min(B, T) non-empty sequences, each scheduled kvh times.
   const int M = (int)min(M_all, p.max_mtiles);
-  if (threadIdx.x == 0) sbase[p.B] = (int32_t)M_all;
+  if (threadIdx.x == 0) sbase[SB] = (int32_t)M_all;
   __syncthreads();
   // C. Every query tile: its sequence (last b with sbase[b] <= i), rows, key
   // range and KV tile count; then the count's prefix sum into u0.
   for (int i = threadIdx.x; i < M; i += kSchedThreads) {
-    int lo = 0, hi = p.B - 1;
+    int lo = 0, hi = SB - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (sbase[mid] <= i) lo = mid; else hi = mid - 1;
@@ -326,7 +331,8 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   for (int i = threadIdx.x; i < M; i += kSchedThreads) {
     const int b = tb[i];
     MTile t;
-    t.b = b;
+    t.b = b / p.kvh;
+    t.kvg = b - t.b * p.kvh;
     t.row0 = trow[2 * i];
     t.nrows = trow[2 * i + 1];
     t.kv_lo = tkv[2 * i];
@@ -334,7 +340,6 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     t.unit0 = u0[i];
     t.tok0 = tlo[b];
     t.past = pst[b];
-    t.pad = 0;
     if (p.split_kv) {
       const int64_t Vi = u0[i] + alpha * i, Vn = u0[i + 1] + alpha * (i + 1);
       const int Wi = cnt(Vi), Wn = cnt(Vn);
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     }
     return;
   }
-  if (sched_ints(p.B, p.max_mtiles, p.grid) <= kSchedLdsInts) schedule_build<true>(p, (int32_t*)lds);
+  if (sched_ints(p.B * p.kvh, p.max_mtiles, p.grid) <= kSchedLdsInts) schedule_build<true>(p, (int32_t*)lds);
   else schedule_build<false>(p, (int32_t*)lds);
 }
 
@@ -404,38 +409,53 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 // Instance table
 // ---------------------------------------------------------------------------
 
-PA_DECLARE_ATTN_INSTANCE(bf16, 576, 512, 4, 32)
-PA_DECLARE_ATTN_INSTANCE(f16, 576, 512, 4, 32)
-PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 4, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 4, 64)
-PA_DECLARE_ATTN_INSTANCE(bf16, 192, 128, 1, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 192, 128, 1, 64)
-PA_DECLARE_ATTN_INSTANCE(bf16, 64, 32, 1, 32)
-PA_DECLARE_ATTN_INSTANCE(f16, 64, 32, 1, 32)
-PA_DECLARE_ATTN_INSTANCE(bf16, 64, 32, 4, 64)
-PA_DECLARE_ATTN_INSTANCE(f16, 64, 32, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, bf16, 576, 512, 4, 32)
+PA_DECLARE_ATTN_INSTANCE(lat, f16, 576, 512, 4, 32)
+PA_DECLARE_ATTN_INSTANCE(lat, bf16, 192, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, f16, 192, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, bf16, 192, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, f16, 192, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, bf16, 64, 32, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(lat, f16, 64, 32, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(lat, bf16, 64, 32, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(lat, f16, 64, 32, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, bf16, 128, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, f16, 128, 128, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, bf16, 128, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, f16, 128, 128, 1, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, bf16, 64, 64, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(sep, f16, 64, 64, 1, 32)
+PA_DECLARE_ATTN_INSTANCE(sep, bf16, 64, 64, 4, 64)
+PA_DECLARE_ATTN_INSTANCE(sep, f16, 64, 64, 4, 64)
 
 struct InstanceEntry {
-  int dtype, hsp, vhsp, nw, kt;
+  int dtype, sep, hsp, vhsp, nw, kt;
   AttnLaunchFn launch;
   AttnOccFn occ;
 };
 
-#define PA_ENTRY(DTC, DTN, HSP, VHSP, NW, KT)                                               \
-  {DTC, HSP, VHSP, NW, KT, &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, launch),                     \
-   &PA_ATTN_FN(DTN, HSP, VHSP, NW, KT, occ)}
+#define PA_SEPV_lat 0
+#define PA_SEPV_sep 1
+#define PA_ENTRY(LAY, DTC, DTN, HSP, VHSP, NW, KT)                                          \
+  {DTC, PA_SEPV_##LAY, HSP, VHSP, NW, KT, &PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, launch), \
+   &PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, occ)}
 
 static const InstanceEntry kInstances[] = {
-    PA_ENTRY(16, bf16, 576, 512, 4, 32),  PA_ENTRY(10, f16, 576, 512, 4, 32),
-    PA_ENTRY(16, bf16, 192, 128, 4, 64), PA_ENTRY(10, f16, 192, 128, 4, 64),
-    PA_ENTRY(16, bf16, 192, 128, 1, 64), PA_ENTRY(10, f16, 192, 128, 1, 64),
-    PA_ENTRY(16, bf16, 64, 32, 1, 32),   PA_ENTRY(10, f16, 64, 32, 1, 32),
-    PA_ENTRY(16, bf16, 64, 32, 4, 64),   PA_ENTRY(10, f16, 64, 32, 4, 64),
+    PA_ENTRY(lat, 16, bf16, 576, 512, 4, 32), PA_ENTRY(lat, 10, f16, 576, 512, 4, 32),
+    PA_ENTRY(lat, 16, bf16, 192, 128, 4, 64), PA_ENTRY(lat, 10, f16, 192, 128, 4, 64),
+    PA_ENTRY(lat, 16, bf16, 192, 128, 1, 64), PA_ENTRY(lat, 10, f16, 192, 128, 1, 64),
+    PA_ENTRY(lat, 16, bf16, 64, 32, 1, 32),   PA_ENTRY(lat, 10, f16, 64, 32, 1, 32),
+    PA_ENTRY(lat, 16, bf16, 64, 32, 4, 64),   PA_ENTRY(lat, 10, f16, 64, 32, 4, 64),
+    PA_ENTRY(sep, 16, bf16, 128, 128, 4, 64), PA_ENTRY(sep, 10, f16, 128, 128, 4, 64),
+    PA_ENTRY(sep, 16, bf16, 128, 128, 1, 64), PA_ENTRY(sep, 10, f16, 128, 128, 1, 64),
+    PA_ENTRY(sep, 16, bf16, 64, 64, 1, 32),   PA_ENTRY(sep, 10, f16, 64, 64, 1, 32),
+    PA_ENTRY(sep, 16, bf16, 64, 64, 4, 64),   PA_ENTRY(sep, 10, f16, 64, 64, 4, 64),
 };
 
 static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
   for (const auto& e : kInstances)
-    if (e.dtype == dtype && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.nw && e.kt == c.kt) return &e;
+    if (e.dtype == dtype && e.sep == c.sep && e.hsp == c.hsp && e.vhsp == c.vhsp && e.nw == c.nw && e.kt == c.kt)
+      return &e;
   return nullptr;
 }
 
@@ -443,12 +463,22 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
   cfg->wide = 0;
   cfg->piece_units = 2;
+  cfg->sep = g.sep;
+  // Query rows per scheduled sequence (per key/value head in the separate layout).
+  const int64_t rows_per_seq = g.B > 0 ? (g.T * (g.H / g.kvh)) / g.B : 0;
+  if (g.sep) {
+    if (g.hs <= 64 && g.vhs <= 64) { cfg->hsp = 64; cfg->vhsp = 64; }
+    else if (g.hs <= 128 && g.vhs <= 128) { cfg->hsp = 128; cfg->vhsp = 128; }
+    else return false;
+    cfg->nw = rows_per_seq >= 96 ? 4 : 1;
+    cfg->kt = (cfg->hsp == 64 && cfg->nw == 1) ? 32 : 64;
+    return find_instance(g.dtype, *cfg) != nullptr;
+  }
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
   else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 10; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
-  const int64_t rows_per_seq = g.B > 0 ? (g.T * g.H) / g.B : 0;
   if (!cfg->wide) cfg->nw = rows_per_seq >= 96 ? 4 : 1;
   if (cfg->hsp == 64 && cfg->nw == 4) cfg->kt = 64;   // staged query rows need 2 tiles >= 32 * nw rows
   return find_instance(g.dtype, *cfg) != nullptr;
@@ -456,8 +486,8 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
 
 hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, int* blocks_per_cu) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, int, int, int>, int> cache;
-  const auto key = std::make_tuple(device, g.dtype, cfg.hsp, cfg.vhsp, cfg.nw, cfg.kt);
+  static std::map<std::tuple<int, int, int, int, int, int, int>, int> cache;
+  const auto key = std::make_tuple(device, g.dtype, cfg.sep, cfg.hsp, cfg.vhsp, cfg.nw, cfg.kt);
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
@@ -480,7 +510,9 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv) {
   WsLayout L{};
   const int RW = cfg.rows();
-  L.max_mtiles = (g.T * g.H + RW - 1) / RW + std::min<int64_t>(g.B, g.T);
+  // Query tiles: T * H rows over the scheduled sequences (each sequence once per
+  // key/value head), at most one partial tile per non-empty scheduled sequence.
+  L.max_mtiles = (g.T * g.H + RW - 1) / RW + std::min<int64_t>(g.B, g.T) * g.kvh;
   const int64_t g_split = (int64_t)num_cus * blocks_per_cu;
   L.grid = (int)(split_kv ? g_split : std::max<int64_t>(L.max_mtiles, 1));
   L.ranges = L.grid;
@@ -489,7 +521,7 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
   L.off_header = off; off = align256(off + 16 * sizeof(int32_t));
   L.off_wg_range = off; off = align256(off + (size_t)(L.ranges + 1) * sizeof(int32_t));
   L.off_wg_tile = off; off = align256(off + (size_t)L.ranges * sizeof(int32_t));
-  L.sched_ints = sched_ints(g.B, L.max_mtiles, L.ranges);
+  L.sched_ints = sched_ints(g.B * g.kvh, L.max_mtiles, L.ranges);
   L.off_sched = off; off = align256(off + (size_t)L.sched_ints * sizeof(int32_t));
   L.off_mtiles = off; off = align256(off + (size_t)(L.max_mtiles + 1) * sizeof(MTile));
   L.off_part_ml = off; off = align256(off + (size_t)L.part_cap * RW * 2 * sizeof(float));
@@ -510,9 +542,10 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
 }
 
 hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
-                            const void* query, const void* cache, const void* cos_t, const void* sin_t,
-                            const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* out,
-                            void* workspace, hipStream_t stream, const hipEvent_t* ev) {
+                            const void* query, const void* cache, const void* value_cache, const void* cos_t,
+                            const void* sin_t, const int32_t* cumseq, const int32_t* past,
+                            const int32_t* block_table, void* out, void* workspace, hipStream_t stream,
+                            const hipEvent_t* ev) {
   if (g.T == 0) return hipSuccess;
   const InstanceEntry* e = find_instance(g.dtype, cfg);
   if (!e) return hipErrorInvalidValue;
@@ -522,7 +555,8 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.past = past;
   sp.B = g.B;
   sp.max_pos = (int)((int64_t)g.MB * g.bs);
-  sp.H = g.H;
+  sp.kvh = g.kvh;
+  sp.H = g.H / g.kvh;
   sp.RW = cfg.rows();
   sp.KT = cfg.kt;
   sp.window = g.window;
@@ -575,7 +609,11 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.qfrag = sp.qfrag;
   ap.nblk = (int)g.NB;   // NB * block_size <= INT32_MAX (checked by the entry points)
   ap.prow = g.do_rotary ? g.P : 1;
-  ap.H = g.H;
+  ap.vcache = (const uint16_t*)value_cache;
+  ap.H = g.H / g.kvh;
+  ap.Hq = g.H;
+  ap.krs = g.kvh * g.hs;
+  ap.vrs = g.kvh * g.vhs;
   ap.hs = g.hs;
   ap.vhs = g.vhs;
   ap.bs_log2 = g.bs_log2;

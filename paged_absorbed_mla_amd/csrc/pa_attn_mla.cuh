@@ -891,11 +891,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 #define PA_DEFINE_ATTN_MLA_INSTANCE(DT, DTN, HSP, VHSP)                                                 \
   namespace pa {                                                                                        \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, occ)(int* n) {                                           \
+  hipError_t PA_ATTN_FN(lat, DTN, HSP, VHSP, 4, 32, occ)(int* n) {                                           \
     void (*fn)(AttnParams) = attn_mla_kernel<DT, HSP, VHSP>;                                            \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), 256, 0);  \
   }                                                                                                     \
-  hipError_t PA_ATTN_FN(DTN, HSP, VHSP, 4, 32, launch)(const AttnParams& p, int grid, bool combine,      \
+  hipError_t PA_ATTN_FN(lat, DTN, HSP, VHSP, 4, 32, launch)(const AttnParams& p, int grid, bool combine,      \
                                                        int cgrid, hipStream_t s, const hipEvent_t* ev) { \
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                          \
     if (e != hipSuccess) return e;                                                                      \

@@ -18,12 +18,14 @@ struct CallGeom {
   int64_t T;
   int B, MB;
   int64_t NB, P;
+  int sep;              // 1: separate (grouped-query) layout with a value cache; 0: latent
+  int kvh;              // key/value heads (1 in the latent layout); H is a multiple of it
 };
 
-// Write phase: one launch.
-hipError_t launch_write(const CallGeom& g, const void* key, const void* cos_t, const void* sin_t,
-                        const int32_t* slot, const int32_t* cumseq, const int32_t* past, void* cache,
-                        hipStream_t stream);
+// Write phase: one launch per cache (value / value_cache: separate layout only, else null).
+hipError_t launch_write(const CallGeom& g, const void* key, const void* value, const void* cos_t,
+                        const void* sin_t, const int32_t* slot, const int32_t* cumseq, const int32_t* past,
+                        void* cache, void* value_cache, hipStream_t stream);
 
 // Attention kernel configuration chosen for a call.
 struct AttnConfig {
@@ -33,6 +35,7 @@ struct AttnConfig {
   int wide;        // 0: attn_kernel (32 rows per wave);
                    // 2: attn_mla_kernel (4 waves x 32 rows, query resident in registers)
   int piece_units; // scheduling cost of one extra piece (query load and epilogue), in KV tiles
+  int sep;         // separate-layout instance (value rows from the value cache)
   int rows() const { return wide ? 128 : 32 * nw; }
 };
 
@@ -61,8 +64,9 @@ WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, i
 // Attention phase: schedule, attention, combine (three launches). `ev`: null, or
 // two events recorded right before and after the attention kernel's launch.
 hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
-                            const void* query, const void* cache, const void* cos_t, const void* sin_t,
-                            const int32_t* cumseq, const int32_t* past, const int32_t* block_table,
-                            void* out, void* workspace, hipStream_t stream, const hipEvent_t* ev);
+                            const void* query, const void* cache, const void* value_cache, const void* cos_t,
+                            const void* sin_t, const int32_t* cumseq, const int32_t* past,
+                            const int32_t* block_table, void* out, void* workspace, hipStream_t stream,
+                            const hipEvent_t* ev);
 
 }  // namespace pa

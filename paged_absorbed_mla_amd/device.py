@@ -16,7 +16,14 @@ def dtype_code(dtype: str) -> int:
 
 
 def attrs_of(w: dict) -> "_lib.pa_latent_attrs":
-    return _lib.make_attrs(**w["attrs"])
+    a = {k: v for k, v in w["attrs"].items() if k not in ("kv_cache_layout", "kv_num_heads")}
+    return _lib.make_attrs(**a)
+
+
+def kv_heads_of(w: dict) -> int:
+    """Key/value heads of a separate-layout workload, 0 for the latent layout."""
+    a = w["attrs"]
+    return int(a["kv_num_heads"]) if a.get("kv_cache_layout") == "SEPARATE" else 0
 
 
 def dims_of(w: dict) -> "_lib.pa_latent_dims":
@@ -40,9 +47,12 @@ class DeviceWorkload:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.device)
 
+        self.kvh = kv_heads_of(w)
         self.query = u16(w["query"])
         self.key = u16(w["key"])
         self.key_cache = u16(w["key_cache"])
+        self.value = u16(w["value"]) if self.kvh else None
+        self.value_cache = u16(w["value_cache"]) if self.kvh else None
         rd = w["attrs"]["rotary_dim"]
         self.cos = u16(w["cos_cache"]) if rd else None
         self.sin = u16(w["sin_cache"]) if rd else None
@@ -60,15 +70,30 @@ class DeviceWorkload:
         self.ws_bytes = 0
         self.workspace = None
         if workspace:
-            self.ws_bytes = _lib.pa_latent_workspace_size(self.attrs, self.dims, self.code,
-                                                          self.device.index or 0)
+            if self.kvh:
+                self.ws_bytes = _lib.pa_separate_workspace_size(self.attrs, self.kvh, self.dims, self.code,
+                                                                self.device.index or 0)
+            else:
+                self.ws_bytes = _lib.pa_latent_workspace_size(self.attrs, self.dims, self.code,
+                                                              self.device.index or 0)
             self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
     def write(self, stream=None):
+        if self.kvh:
+            return _lib.pa_separate_write(self.attrs, self.kvh, self.dims, self.code, self.key, self.value,
+                                          self.cos, self.sin, self.slot_mapping, self.cumseq, self.past,
+                                          self.key_cache, self.value_cache, stream)
         return _lib.pa_latent_write(self.attrs, self.dims, self.code, self.key, self.cos, self.sin,
                                     self.slot_mapping, self.cumseq, self.past, self.key_cache, stream)
 
     def attention(self, stream=None, split_kv: Optional[bool] = None):
+        if self.kvh:
+            if split_kv is not None:
+                raise ValueError("the separate layout has no forced split-KV entry point")
+            return _lib.pa_separate_attention(self.attrs, self.kvh, self.dims, self.code, self.query,
+                                              self.key_cache, self.value_cache, self.cos, self.sin, self.cumseq,
+                                              self.past, self.block_table, self.output, self.workspace,
+                                              self.ws_bytes, stream)
         if split_kv is None:
             return _lib.pa_latent_attention(self.attrs, self.dims, self.code, self.query, self.key_cache,
                                             self.cos, self.sin, self.cumseq, self.past, self.block_table,
@@ -86,6 +111,10 @@ class DeviceWorkload:
     def cache_bits(self) -> np.ndarray:
         import torch
         return self.key_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def value_cache_bits(self) -> np.ndarray:
+        import torch
+        return self.value_cache.view(torch.int16).cpu().numpy().view(np.uint16)
 
     def output_f64(self) -> np.ndarray:
         import torch

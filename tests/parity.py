@@ -86,3 +86,34 @@ def swap_heads(out: np.ndarray, heads: int, a: int = 0, b: int = 1) -> np.ndarra
 def oracle(w: dict, tokens=None):
     cache = orc.write_phase(w)
     return cache, orc.attention(w, cache, tokens=tokens)
+
+
+def check_write_separate(w: dict, gpu_k: np.ndarray, gpu_v: np.ndarray, ref_k: np.ndarray, ref_v: np.ndarray,
+                         before_k: np.ndarray, before_v: np.ndarray):
+    """Separate layout: both caches, per slot (all key/value heads of a slot).
+    Key rows as in check_write (bit exact outside the rotary channels, 1 ulp
+    inside); value rows bit exact; slots no token writes unchanged."""
+    a = w["attrs"]
+    kvh, hs = a["kv_num_heads"], a["head_size"]
+    vhs = a["v_head_size"] or hs
+    gk, rk, bk = (x.reshape(-1, kvh, hs) for x in (gpu_k, ref_k, before_k))
+    gv, rv, bv = (x.reshape(-1, kvh, vhs) for x in (gpu_v, ref_v, before_v))
+    slots = w["slot_mapping"]
+    written = np.unique(slots[slots >= 0])
+    untouched = np.setdiff1d(np.arange(gk.shape[0]), written)
+    assert np.array_equal(gk[untouched], bk[untouched]), "key slots without a token changed"
+    assert np.array_equal(gv[untouched], bv[untouched]), "value slots without a token changed"
+    assert np.array_equal(gv[written], rv[written]), "written value rows differ"
+    rot = np.zeros(hs, dtype=bool)
+    if a["do_rotary"]:
+        rot[a["rotary_offset"]:a["rotary_offset"] + a["rotary_dim"]] = True
+    kw, kr = gk[written], rk[written]
+    assert np.array_equal(kw[..., ~rot], kr[..., ~rot]), "non-rotary channels of written key rows differ"
+    if rot.any():
+        d = ulp_distance(kw[..., rot], kr[..., rot])
+        assert d.max() <= 1, f"rotary channels differ by {d.max()} ulp"
+
+
+def oracle_separate(w: dict, tokens=None):
+    from oracle import paged_separate as sep
+    return sep.run(w, tokens=tokens)

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pa.pa_latent_abi_version() == 1
+    assert pa.pa_latent_abi_version() == 2
 
 
 def glm_attrs(**kw):
@@ -158,3 +158,76 @@ def test_binding_raises_with_message():
     with pytest.raises(pa.PaError, match="power of two"):
         pa.pa_latent_write(glm_attrs(block_size=24), dims(), pa.PA_BF16, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
                            DUMMY, DUMMY, stream=0)
+
+
+# ----------------------------------------------------------------------------
+# Separate (grouped-query) layout: the head-ratio rule of PR #1940's third
+# commit (num_heads % kv_num_heads, rejection case 4/3), the value inputs, and
+# the head sizes built for it.
+# ----------------------------------------------------------------------------
+
+def gqa_attrs(**kw):
+    base = dict(num_heads=32, head_size=128, v_head_size=128, block_size=16, do_rotary=1,
+                rotary_interleaved=0, rotary_dim=128, rotary_offset=0, local_window_size=-1,
+                softcap=0.0, has_scale=0, scale=0.0)
+    base.update(kw)
+    return pa.make_attrs(**base)
+
+
+def sep_attn(a, kvh, d=None, ptrs=None, ws=DUMMY, ws_bytes=1 << 30):
+    p = dict(query=DUMMY, key_cache=DUMMY, value_cache=DUMMY, cos=DUMMY, sin=DUMMY, cumseq=DUMMY, past=DUMMY,
+             bt=DUMMY, out=DUMMY)
+    p.update(ptrs or {})
+    return pa.pa_separate_attention(a, kvh, d or dims(), pa.PA_BF16, p["query"], p["key_cache"], p["value_cache"],
+                                    p["cos"], p["sin"], p["cumseq"], p["past"], p["bt"], p["out"], ws, ws_bytes,
+                                    stream=0, check=False)
+
+
+def sep_write(a, kvh, d=None, ptrs=None):
+    p = dict(key=DUMMY, value=DUMMY, cos=DUMMY, sin=DUMMY, slot=DUMMY, cumseq=DUMMY, past=DUMMY, cache=DUMMY,
+             vcache=DUMMY)
+    p.update(ptrs or {})
+    return pa.pa_separate_write(a, kvh, d or dims(), pa.PA_BF16, p["key"], p["value"], p["cos"], p["sin"],
+                                p["slot"], p["cumseq"], p["past"], p["cache"], p["vcache"], stream=0, check=False)
+
+
+SEP_CASES = [
+    ("ratio 4/3", dict(num_heads=4), 3, pa.PA_ERR_INVALID_ARGUMENT, "multiple of kv_num_heads"),
+    ("ratio 32/5", {}, 5, pa.PA_ERR_INVALID_ARGUMENT, "multiple of kv_num_heads"),
+    ("zero kv heads", {}, 0, pa.PA_ERR_INVALID_ARGUMENT, "kv_num_heads"),
+    ("more kv heads than heads", dict(num_heads=4), 8, pa.PA_ERR_INVALID_ARGUMENT, "multiple of kv_num_heads"),
+    ("v_head_size % 8", dict(v_head_size=100, has_scale=1, scale=0.1), 8, pa.PA_ERR_NOT_IMPLEMENTED,
+     "multiple of 8"),
+    ("block_size 8", dict(block_size=8), 8, pa.PA_ERR_INVALID_ARGUMENT, "power of two >= 16"),
+]
+
+
+@pytest.mark.parametrize("desc,akw,kvh,status,frag", SEP_CASES, ids=[c[0] for c in SEP_CASES])
+def test_separate_rejections_before_launch(desc, akw, kvh, status, frag):
+    a = gqa_attrs(**akw)
+    for fn in (sep_attn, sep_write):
+        st = fn(a, kvh)
+        assert st == status, (desc, fn.__name__, pa.pa_last_error())
+        assert frag in pa.pa_last_error(), pa.pa_last_error()
+
+
+@pytest.mark.parametrize("H,kvh", [(4, 2), (4, 4), (32, 8), (32, 1)])
+def test_separate_accepts_valid_ratios(H, kvh):
+    # valid ratios pass every check and stop only at the (NULL) workspace
+    assert sep_attn(gqa_attrs(num_heads=H), kvh, ws=None) == pa.PA_ERR_INVALID_ARGUMENT
+    assert "workspace" in pa.pa_last_error()
+
+
+def test_separate_needs_value_inputs():
+    assert sep_attn(gqa_attrs(), 8, ptrs={"value_cache": None}) == pa.PA_ERR_INVALID_ARGUMENT
+    assert "value_cache" in pa.pa_last_error()
+    assert sep_write(gqa_attrs(), 8, ptrs={"value": None}) == pa.PA_ERR_INVALID_ARGUMENT
+    assert "'value'" in pa.pa_last_error()
+    assert sep_write(gqa_attrs(), 8, ptrs={"vcache": None}) == pa.PA_ERR_INVALID_ARGUMENT
+    assert "value_cache" in pa.pa_last_error()
+
+
+def test_separate_head_size_without_instance_is_not_implemented():
+    a = gqa_attrs(head_size=192, v_head_size=128, rotary_dim=64, has_scale=1, scale=0.07)
+    assert sep_attn(a, 8) == pa.PA_ERR_NOT_IMPLEMENTED
+    assert "separate layout" in pa.pa_last_error()

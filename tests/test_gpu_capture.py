@@ -83,3 +83,39 @@ def test_capture_of_an_unwarmed_signature_is_refused():
     d.attention()
     torch.cuda.synchronize()
     assert _lib.pa_latent_capture_ready(d.attrs, d.dims, d.code) == (True, True)
+
+
+def test_capture_separate_layout_three_replays_bit_equal_to_eager():
+    """The separate (grouped-query) entry points under the same gate: after an
+    eager step the capture replays bit-equal; a different kv_num_heads is a
+    different signature and is refused."""
+    torch = _torch()
+    w = wl.make("gqa_decode", scale_down=4)
+    d = _dev(w)
+    before_k, before_v = d.key_cache.clone(), d.value_cache.clone()
+    d.write()
+    d.attention()
+    torch.cuda.synchronize()
+    eager = (_bits(d.output), _bits(d.key_cache), _bits(d.value_cache))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.write()
+        d.attention()
+    for rep in range(3):
+        d.key_cache.copy_(before_k)
+        d.value_cache.copy_(before_v)
+        d.output.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (_bits(d.output), _bits(d.key_cache), _bits(d.value_cache))
+        for name, a, b in zip(("output", "key cache", "value cache"), got, eager):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs"
+    del g
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        st = _lib.pa_separate_attention(d.attrs, d.kvh // 2, d.dims, d.code, d.query, d.key_cache, d.value_cache,
+                                        d.cos, d.sin, d.cumseq, d.past, d.block_table, d.output, d.workspace,
+                                        d.ws_bytes, check=False)
+    assert st == _lib.PA_ERR_CAPTURE_NOT_WARMED
+    del g2
