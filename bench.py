@@ -42,6 +42,10 @@ WORKLOADS = {
     "c3": "glm_192_128_64_chunked_prefill_f16_4x1024",
     "c5": "mixed_576_512_64_f16_window1024_softcap50",
     "c1": "tiny_64_32_16_prefill_decode_f16",
+    # grouped-query (separate cache layout) workloads: 32 query heads over 8 key/value heads, 128/128
+    "gqa_decode": "gqa_128_32q8kv_decode_bf16_b32_ctx512-4k",
+    "gqa_prefill": "gqa_128_32q8kv_chunked_prefill_f16_4x1024",
+    "gqa_tiny": "gqa_tiny_64_64_4q2kv_prefill_decode_f16",
 }
 
 
@@ -95,6 +99,8 @@ def attention_kernel_name(w: dict) -> str:
     four-wave 576/512 kernel for rows wider than 192 channels, else the
     generic one."""
     a = w["attrs"]
+    if a.get("kv_cache_layout") == "SEPARATE":
+        return "attn_kernel"
     return DOMINANT_KERNEL if a["head_size"] > 192 or a["v_head_size"] > 128 else "attn_kernel"
 
 
@@ -243,7 +249,7 @@ def cpu_baseline(w, target_s: float):
     workload until about target_s seconds of work, scaled to TFLOP/s."""
     import numpy as np
     from oracle import paged_latent as orc
-    from paged_absorbed_mla_amd import workloads as wl
+    from oracle import paged_separate as sep
 
     try:
         from threadpoolctl import threadpool_info
@@ -256,13 +262,14 @@ def cpu_baseline(w, target_s: float):
     B = len(cum) - 1
     done_flops = 0
     done_tokens = 0
+    separate = a.get("kv_cache_layout") == "SEPARATE"
     t0 = time.perf_counter()
-    cache = orc.write_phase(w)
+    caches = sep.write_phase(w) if separate else (orc.write_phase(w),)
     b = 0
     while b < B and time.perf_counter() - t0 < target_s:
         toks = np.arange(cum[b], cum[b + 1])
         if toks.size:
-            orc.attention(w, cache, tokens=toks)
+            (sep.attention if separate else orc.attention)(w, *caches, tokens=toks)
             for t in toks:
                 pos = int(w["past_seqlens"][b]) + int(t - cum[b])
                 lo = 0 if a["local_window_size"] < 0 else max(0, pos - a["local_window_size"])
@@ -457,7 +464,7 @@ def main():
         "kernel_ms": stats(kern_ms),
         "alg_bytes_per_launch": int(byts), "alg_flops_per_launch": int(flops),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-        "phase": dict({"what": "pa_latent_attention: schedule launch + attention kernel + combine (events around "
+        "phase": dict({"what": "attention call: schedule launch + attention kernel + combine (events around "
                                "the call)", "avg_ms": round(attn_avg_ms, 5), "ms": stats(attn_ms)},
                       **side(attn_avg_ms)),
         "step": dict({"what": f"write + attention, whole-job time / steps ({args.launch} launch)",
@@ -483,6 +490,7 @@ def main():
                    "batch": w["dims"]["batch"], "num_heads": w["attrs"]["num_heads"],
                    "head_size": w["attrs"]["head_size"], "v_head_size": w["attrs"]["v_head_size"],
                    "block_size": w["attrs"]["block_size"], "kv_rows": counts["kv_rows"],
+                   **({"kv_num_heads": w["attrs"]["kv_num_heads"]} if "kv_num_heads" in w["attrs"] else {}),
                    "tokens_per_s": round(w["dims"]["token_count"] / (ms_step * 1e-3), 1)},
         "roofline": roof,
     }
