@@ -109,8 +109,8 @@ pa_status resolve(const pa_latent_attrs* a, const pa_latent_dims* d, pa_dtype dt
     return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks * block_size exceeds the int32 slot range");
   if (sep && (int64_t)d->batch * kv_num_heads > (int64_t)INT32_MAX / 8)
     return fail(PA_ERR_INVALID_ARGUMENT, "batch * kv_num_heads exceeds the schedule's range");
-  if (sep && d->num_blocks * (int64_t)bs * kv_num_heads * hs > (int64_t)INT32_MAX * 64)
-    return fail(PA_ERR_INVALID_ARGUMENT, "key cache exceeds the addressable range");
+  if (sep && (int64_t)bs * kv_num_heads * hs * 2 > (int64_t)INT32_MAX / 2)
+    return fail(PA_ERR_INVALID_ARGUMENT, "block_size * kv_num_heads * head_size exceeds a cache block's range");
   g->dtype = (int)dtype;
   g->H = a->num_heads;
   g->hs = hs;

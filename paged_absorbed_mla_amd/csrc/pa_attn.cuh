@@ -190,6 +190,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// One 16-byte-per-lane direct global->LDS copy: lane l's 16 bytes at buffer
+// offset voff land at LDS address lds_base + 16 l. Issued as inline assembly
+// so that the compiler does not see an LDS write it cannot order: it would
+// otherwise drain every in-flight copy (vmcnt(0)) before the next LDS read.
+// The caller orders copies against LDS reads with explicit vmcnt waits and a
+// barrier. `rsrc` is a raw buffer descriptor (loads past its size read zeros).
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, uint32_t voff, u32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// Raw buffer descriptor words over `bytes` bytes at `base` (stride 0, the same
+// descriptor make_rsrc builds).
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// rsrc_words for a wave-uniform base: the words are forced into SGPRs.
+__device__ __forceinline__ u32x4_t rsrc_words_u(const void* base, uint32_t bytes) {
+  u32x4_t r = rsrc_words(base, bytes);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = __builtin_amdgcn_readfirstlane(r[k]);
+  return r;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -451,7 +477,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
 // from the value cache into a second part of each LDS buffer; otherwise V is
 // the leading VHSP channels of the latent row already in the buffer.
 template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG, bool SEP>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1))) void attn_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;          // 16-byte chunks per LDS row
   constexpr int VCPR = SEP ? VHSP / 8 : CPR;
@@ -473,8 +499,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   constexpr int QSTRIDE = QREG + 8;     // staged rows padded by 16 bytes against bank conflicts
   constexpr int QRS = HSP - QREG + 8;
   constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
+  // Tile buffers: NBUF - 1 tiles are in flight while one is computed. Four
+  // waves get four buffers; a one-wave workgroup keeps two, so that several
+  // workgroups still fit in a CU's LDS.
+  constexpr int NBUF = 2;
+  constexpr int PER = LOADS + VLOADS;   // copy instructions per wave and tile (vmcnt counts them)
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
-  constexpr int KV_BYTES = (2 * BUF_BYTES > QSTAGE_BYTES) ? 2 * BUF_BYTES : QSTAGE_BYTES;
+  constexpr int KV_BYTES = (NBUF * BUF_BYTES > QSTAGE_BYTES) ? NBUF * BUF_BYTES : QSTAGE_BYTES;
   constexpr int QREST_BYTES = (QREG < HSP) ? RW * QRS * 2 : 0;
   constexpr int LDS_BYTES = KV_BYTES + QREST_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -494,23 +525,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
   const int i_first = i;
   const bool softcap_on = p.softcap > 0.0f;
-  // Byte offset, within its cache block, of the 16-byte chunk each lane copies
-  // in copy instruction `it` (tile-independent).
-  int load_off[LOADS];
+  // Byte offset, from the first key of its cache block in the tile, of the
+  // 16-byte chunk each lane copies in copy instruction `it` (tile-independent);
+  // chunks past the head (padded head sizes) get an offset past every
+  // descriptor and land as zeros.
+  uint32_t load_off[LOADS];
 #pragma unroll
   for (int it = 0; it < LOADS; ++it) {
     const int pidx = it * NT + (int)threadIdx.x;
     const int k = pidx / CPR;
     const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-    load_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.krs + lc * 8) * 2;
+    load_off[it] = lc * 8 < p.hs ? (uint32_t)(((k & ((1 << p.bs_log2) - 1)) * p.krs + lc * 8) * 2) : kOutOfRange;
   }
-  int vload_off[VLOADS > 0 ? VLOADS : 1];
+  uint32_t vload_off[VLOADS > 0 ? VLOADS : 1];
 #pragma unroll
   for (int it = 0; it < VLOADS; ++it) {
     const int pidx = it * NT + (int)threadIdx.x;
     const int k = pidx / VCPR;
     const int lc = (pidx - k * VCPR) ^ lds_swizzle(k);
-    vload_off[it] = ((k & ((1 << p.bs_log2) - 1)) * p.vrs + lc * 8) * 2;
+    vload_off[it] = lc * 8 < p.vhs ? (uint32_t)(((k & ((1 << p.bs_log2) - 1)) * p.vrs + lc * 8) * 2) : kOutOfRange;
   }
 
   const int n_tiles = ld_uniform(p.header + 1);   // query tiles of the schedule
@@ -588,95 +621,86 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     st.m_run = -INFINITY;
     st.l_run = 0.0f;
 
-    // Copy KV tile `tile` into LDS buffer `bufi`: 16 bytes per lane, global ->
-    // LDS directly. Copy instruction (it, wave) fills 64 consecutive 16-byte
-    // LDS slots, which always belong to rows of one cache block (block_size *
-    // CPR is a multiple of 64), so its source is a scalar block base plus the
-    // lane's precomputed offset. Slots of keys outside [kv_lo, kv_hi) or
-    // channels >= hs are zero-filled instead (boundary tiles only).
+    // Copy KV tile `tile` into LDS buffer `bufi`: exactly PER copy
+    // instructions per wave (LOADS for K rows, VLOADS for V rows), 16 bytes per
+    // lane, global -> LDS directly. Copy instruction (it, wave) fills 64
+    // consecutive 16-byte LDS slots, which always belong to rows of one cache
+    // block (block_size * CPR is a multiple of 64). Each block of the tile gets
+    // a descriptor over its keys below kv_hi, so later keys land as zeros;
+    // keys below kv_lo (the first tile of a windowed range) take an
+    // out-of-range offset per lane.
+    const uint32_t lds0 = lds_addr(lds_raw);
     auto issue = [&](int tile, int bufi) {
       const int key0 = tile * KT;
       const int blk0 = key0 >> p.bs_log2;
       const int in_blk = key0 & ((1 << p.bs_log2) - 1);      // nonzero only when block_size > KT
-      int blks[NBLK];
+      // The tile's block ids: every scalar load goes out before the first use
+      // (one round trip, not one per block).
+      int ids[NBLK];
 #pragma unroll
-      for (int e = 0; e < NBLK; ++e) blks[e] = clamp_block(ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1)), p.nblk);
-      uint8_t* dst0 = lds_raw + bufi * BUF_BYTES + w * 64 * 16;
-      uint8_t* vdst0 = dst0 + TILE_CHUNKS * 16;
-      if (key0 >= t.kv_lo && key0 + KT <= t.kv_hi && p.hs == HSP && (!SEP || p.vhs == VHSP)) {
-        // Interior tile: every slot is a real cache chunk.
+      for (int e = 0; e < NBLK; ++e) ids[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4_t rk[NBLK], rv[NBLK];
 #pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-          const int e = (((it * NW + w) * 64) / CPR) >> p.bs_log2;   // scalar: the slots' block
-          int blk = blks[0];
+      for (int e = 0; e < NBLK; ++e) {
+        const int blk = clamp_block(ids[e], p.nblk);
+        const int first = e == 0 ? in_blk : 0;               // first row of the block in this tile
+        const int kfirst = ((blk0 + e) << p.bs_log2) + first;
+        const int nkeys = min(max(t.kv_hi - kfirst, 0), (1 << p.bs_log2) - first);
+        const int64_t row0 = ((int64_t)blk << p.bs_log2) + first;
+        rk[e] = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
+        if constexpr (SEP)
+          rv[e] = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
+      }
+      const bool lower = key0 < t.kv_lo;
+      const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + w * 64 * 16);
 #pragma unroll
-          for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
-          const uint8_t* base =
-              (const uint8_t*)(p.cache + (((int64_t)blk << p.bs_log2) + in_blk) * p.krs + t.kvg * p.hs);
-          __builtin_amdgcn_global_load_lds(base + load_off[it], dst0 + it * NT * 16, 16, 0, 0);
+      for (int it = 0; it < LOADS; ++it) {
+        const int e = (((it * NW + w) * 64) / CPR) >> p.bs_log2;   // scalar: the slots' block
+        u32x4_t r = rk[0];
+#pragma unroll
+        for (int q = 1; q < NBLK; ++q) r = (e == q) ? rk[q] : r;
+        uint32_t off = load_off[it];
+        if (lower) {
+          const int j = key0 + (it * NT + opaque_lane() + w * 64) / CPR;
+          off = j >= t.kv_lo ? off : kOutOfRange;
         }
+        copy16_to_lds(dst + it * NT * 16, off, r);
+      }
 #pragma unroll
-        for (int it = 0; it < VLOADS; ++it) {
-          const int e = (((it * NW + w) * 64) / VCPR) >> p.bs_log2;
-          int blk = blks[0];
+      for (int it = 0; it < VLOADS; ++it) {
+        const int e = (((it * NW + w) * 64) / VCPR) >> p.bs_log2;
+        u32x4_t r = rv[0];
 #pragma unroll
-          for (int q = 1; q < NBLK; ++q) blk = (e == q) ? blks[q] : blk;
-          const uint8_t* base =
-              (const uint8_t*)(p.vcache + (((int64_t)blk << p.bs_log2) + in_blk) * p.vrs + t.kvg * p.vhs);
-          __builtin_amdgcn_global_load_lds(base + vload_off[it], vdst0 + it * NT * 16, 16, 0, 0);
+        for (int q = 1; q < NBLK; ++q) r = (e == q) ? rv[q] : r;
+        uint32_t off = vload_off[it];
+        if (lower) {
+          const int j = key0 + (it * NT + opaque_lane() + w * 64) / VCPR;
+          off = j >= t.kv_lo ? off : kOutOfRange;
         }
-      } else {
-        // Boundary tile: keys outside [kv_lo, kv_hi) or channels >= hs are zero-filled.
-#pragma unroll 1
-        for (int it = 0; it < LOADS; ++it) {
-          const int pidx = it * NT + (int)threadIdx.x;
-          const int k = pidx / CPR;
-          const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-          const int j = key0 + k;
-          uint8_t* dst = dst0 + it * NT * 16;
-          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.hs) {
-            const int blkv = clamp_block(p.bt[(int64_t)b * p.MB + min(j >> p.bs_log2, p.MB - 1)], p.nblk);
-            const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
-            __builtin_amdgcn_global_load_lds(p.cache + row * p.krs + t.kvg * p.hs + lc * 8, dst, 16, 0, 0);
-          } else {
-            *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
-#pragma unroll 1
-        for (int it = 0; it < VLOADS; ++it) {
-          const int pidx = it * NT + (int)threadIdx.x;
-          const int k = pidx / VCPR;
-          const int lc = (pidx - k * VCPR) ^ lds_swizzle(k);
-          const int j = key0 + k;
-          uint8_t* dst = vdst0 + it * NT * 16;
-          if (j >= t.kv_lo && j < t.kv_hi && lc * 8 < p.vhs) {
-            const int blkv = clamp_block(p.bt[(int64_t)b * p.MB + min(j >> p.bs_log2, p.MB - 1)], p.nblk);
-            const int64_t row = ((int64_t)blkv << p.bs_log2) + (j & ((1 << p.bs_log2) - 1));
-            __builtin_amdgcn_global_load_lds(p.vcache + row * p.vrs + t.kvg * p.vhs + lc * 8, dst, 16, 0, 0);
-          } else {
-            *(u32x4_t*)(dst + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
+        copy16_to_lds(dst + (TILE_CHUNKS + it * NT) * 16, off, r);
       }
     };
 
-    issue(tile_a, 0);
-    if (wave_active) {
-      for (int tt = tile_a; tt < tile_b; ++tt) {
-        const int bufi = (tt - tile_a) & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
+    // Ring of NBUF buffers: tile tt sits in buffer (tt - tile_a) % NBUF; the
+    // first NBUF - 1 tiles go out before the loop, and iteration tt, once every
+    // wave has passed its barrier (so the buffer of tile tt - 1 is free),
+    // issues tile tt + NBUF - 1 into that buffer.
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (tile_a + k < tile_b) issue(tile_a + k, k);
+    for (int tt = tile_a; tt < tile_b; ++tt) {
+      const int bufi = (tt - tile_a) % NBUF;
+      // This wave's copies of tile tt are done once at most (tiles issued
+      // after it) * PER copies remain in flight; the barrier then makes every
+      // wave's copies of tile tt visible.
+      vm_wait_tiles<PER, NBUF - 2>(min(NBUF - 2, tile_b - 1 - tt));
+      lds_barrier();
+      if (tt + NBUF - 1 < tile_b) issue(tt + NBUF - 1, (tt + NBUF - 1 - tile_a) % NBUF);
+      if (wave_active) {
         const uint8_t* buf = lds_raw + bufi * BUF_BYTES;
         tile_compute<DT, HSP, VHSP, KT, QREG, VCPR>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
                                                     pos, lo_row, softcap_on, p);
-      }
-    } else {
-      for (int tt = tile_a; tt < tile_b; ++tt) {
-        const int bufi = (tt - tile_a) & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tt + 1 < tile_b) issue(tt + 1, bufi ^ 1);
       }
     }
     __syncthreads();

@@ -118,24 +118,6 @@ __device__ __forceinline__ void ds_write_b128_v(uint32_t addr, u32x4_t v) {
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
 }
 
-// One 16-byte-per-lane direct global->LDS copy: lane l's 16 bytes at buffer
-// offset voff land at LDS address lds_base + 16 l. Issued as inline assembly
-// so that the compiler does not see an LDS write it cannot order: it would
-// otherwise drain every in-flight copy (vmcnt(0)) before the next LDS read.
-// The caller orders copies against LDS reads with explicit vmcnt waits and a
-// barrier. `rsrc` is a raw buffer descriptor (loads past its size read zeros).
-__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, uint32_t voff, u32x4_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-// Raw buffer descriptor words over `bytes` bytes at `base` (stride 0, the same
-// descriptor make_rsrc builds).
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-
 // s_waitcnt lgkmcnt(N) that also passes `v` through, so every use of `v`
 // (an LDS read issued by inline assembly, invisible to the compiler's own
 // waits) is ordered after the wait.
@@ -155,14 +137,6 @@ __device__ __forceinline__ void lgkm_wait_fence() {
   static_assert(N >= 0 && N < 16, "lgkmcnt field");
   __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
   __builtin_amdgcn_sched_barrier(0);
-}
-
-// rsrc_words for a wave-uniform base: the words are forced into SGPRs.
-__device__ __forceinline__ u32x4_t rsrc_words_u(const void* base, uint32_t bytes) {
-  u32x4_t r = rsrc_words(base, bytes);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) r[k] = __builtin_amdgcn_readfirstlane(r[k]);
-  return r;
 }
 
 // 16-byte buffer load at byte offset voff through descriptor words `rsrc`
