@@ -324,7 +324,7 @@ struct WaveState {
 template <typename DT, int HSP, int VHSP, int KT, int QREG, int VCPR>
 __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>& st, const uint8_t* L,
                                              const uint8_t* LV, const uint16_t* qrest, int key0, int pos,
-                                             int lo_row, bool softcap_on, const AttnParams& p) {
+                                             int lo_row, bool softcap_on, bool full, const AttnParams& p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;
   constexpr int NKK = HSP / 16;
@@ -386,17 +386,32 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
       for (int e = 0; e < 16; ++e) s[sub][e] = softcap_log2(s[sub][e], p.scale, p.softcap, p.softcap_inv);
   } else {
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) s[sub] *= p.scale_log2;
+    for (int sub = 0; sub < NSUB; ++sub) {
+      // Element by element: a vector-times-scalar product would splat the
+      // scalar into 16 registers.
+      const float sc = p.scale_log2;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[sub][e] *= sc;
+    }
   }
+  // `full` (wave-uniform): every row of the wave sees every key of the tile,
+  // so no key is masked.
   float tmax = -INFINITY;
+  if (full) {
 #pragma unroll
-  for (int sub = 0; sub < NSUB; ++sub) {
+    for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = key0 + sub * 32 + hi * 4 + (e & 3) + 8 * (e >> 2);
-      const float v = (j <= pos && j >= lo_row) ? s[sub][e] : -INFINITY;
-      s[sub][e] = v;
-      tmax = fmaxf(tmax, v);
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[sub][e]);
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = key0 + sub * 32 + hi * 4 + (e & 3) + 8 * (e >> 2);
+        const float v = (j <= pos && j >= lo_row) ? s[sub][e] : -INFINITY;
+        s[sub][e] = v;
+        tmax = fmaxf(tmax, v);
+      }
     }
   }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -428,7 +443,9 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   st.l_run = st.l_run * corr + psum;
   if (__any(rescale)) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) st.o[mt] *= corr;
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[mt][e] *= corr;
   }
   // O^T += V^T P^T. Transposing reads: lane (g, jj, cq) supplies key row jj and
   // channel quad cq of its 16-lane group; the group's lane i receives channel i
@@ -489,7 +506,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   constexpr int NKK = HSP / 16;
   constexpr int NMT = VHSP / 32;
   constexpr int RW = NW * 32;
-  constexpr int NBLK = KT / 16;         // most blocks a tile can touch (block_size >= 16)
   static_assert(HSP % 64 == 0 && VHSP % 32 == 0 && VHSP <= HSP, "head sizes");
   static_assert(KT % 32 == 0 && TILE_CHUNKS % NT == 0 && VTILE_CHUNKS % NT == 0, "tile shape");
   static_assert(!SEP || VHSP % 64 == 0, "value rows: whole swizzle periods");
@@ -525,25 +541,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
   const int i_first = i;
   const bool softcap_on = p.softcap > 0.0f;
-  // Byte offset, from the first key of its cache block in the tile, of the
-  // 16-byte chunk each lane copies in copy instruction `it` (tile-independent);
-  // chunks past the head (padded head sizes) get an offset past every
-  // descriptor and land as zeros.
-  uint32_t load_off[LOADS];
+  // Copies move 16-key groups: group g of a tile (keys 16 g .. 16 g + 15)
+  // lies in one cache block (block_size >= 16 and a power of two), so one
+  // descriptor serves all its copy instructions; wave w copies groups
+  // w, w + NW, ... Copy instruction i of a group fills LDS slots
+  // 64 i .. 64 i + 63 of the group's rows. load_off[i]: byte offset, from the
+  // group's first row, of the chunk the lane copies (chunks past the head, for
+  // padded head sizes, get an offset past every descriptor and land as zeros).
+  constexpr int KG = KT / 16;           // key groups per tile
+  constexpr int GPW = KG / NW;          // groups per wave
+  constexpr int IPG = CPR / 4;          // K copy instructions per group (16 rows x CPR chunks / 64)
+  constexpr int VIPG = SEP ? VCPR / 4 : 0;
+  static_assert(KG % NW == 0 && CPR % 4 == 0 && GPW * IPG == LOADS && GPW * VIPG == VLOADS, "copy split");
+  uint32_t load_off[IPG];
 #pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
-    const int pidx = it * NT + (int)threadIdx.x;
-    const int k = pidx / CPR;
-    const int lc = (pidx - k * CPR) ^ lds_swizzle(k);
-    load_off[it] = lc * 8 < p.hs ? (uint32_t)(((k & ((1 << p.bs_log2) - 1)) * p.krs + lc * 8) * 2) : kOutOfRange;
+  for (int i = 0; i < IPG; ++i) {
+    const int pidx = i * 64 + lane;
+    const int kl = pidx / CPR;
+    const int lc = (pidx - kl * CPR) ^ lds_swizzle(kl);
+    load_off[i] = lc * 8 < p.hs ? (uint32_t)((kl * p.krs + lc * 8) * 2) : kOutOfRange;
   }
-  uint32_t vload_off[VLOADS > 0 ? VLOADS : 1];
+  uint32_t vload_off[VIPG > 0 ? VIPG : 1];
 #pragma unroll
-  for (int it = 0; it < VLOADS; ++it) {
-    const int pidx = it * NT + (int)threadIdx.x;
-    const int k = pidx / VCPR;
-    const int lc = (pidx - k * VCPR) ^ lds_swizzle(k);
-    vload_off[it] = lc * 8 < p.vhs ? (uint32_t)(((k & ((1 << p.bs_log2) - 1)) * p.vrs + lc * 8) * 2) : kOutOfRange;
+  for (int i = 0; i < VIPG; ++i) {
+    const int pidx = i * 64 + lane;
+    const int kl = pidx / VCPR;
+    const int lc = (pidx - kl * VCPR) ^ lds_swizzle(kl);
+    vload_off[i] = lc * 8 < p.vhs ? (uint32_t)((kl * p.vrs + lc * 8) * 2) : kOutOfRange;
   }
 
   const int n_tiles = ld_uniform(p.header + 1);   // query tiles of the schedule
@@ -565,6 +589,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     const int pos = row_ok ? past_b + tq : -1;
     const int lo_row = p.window >= 0 ? max(0, pos - p.window) : 0;
     const bool wave_active = w * 32 < t.nrows;
+    // Keys every row of this wave sees: [lo_max_w, pos_min_w] (wave-uniform).
+    const int pos_min_w = past_b + (t.row0 + w * 32) / p.H;
+    const int pos_max_w = past_b + (t.row0 + min(w * 32 + 31, t.nrows - 1)) / p.H;
+    const int lo_max_w = p.window >= 0 ? max(0, pos_max_w - p.window) : 0;
     const int64_t qrow = head_row(p, t, R);
 
     WaveState<DT, HSP, VHSP, KT, QREG> st;
@@ -622,63 +650,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     st.l_run = 0.0f;
 
     // Copy KV tile `tile` into LDS buffer `bufi`: exactly PER copy
-    // instructions per wave (LOADS for K rows, VLOADS for V rows), 16 bytes per
-    // lane, global -> LDS directly. Copy instruction (it, wave) fills 64
-    // consecutive 16-byte LDS slots, which always belong to rows of one cache
-    // block (block_size * CPR is a multiple of 64). Each block of the tile gets
-    // a descriptor over its keys below kv_hi, so later keys land as zeros;
-    // keys below kv_lo (the first tile of a windowed range) take an
-    // out-of-range offset per lane.
+    // instructions per wave (vmcnt counts them), 16 bytes per lane, global ->
+    // LDS directly. A group's descriptor covers its keys below kv_hi, so later
+    // keys land as zeros; keys below kv_lo (the first tile of a windowed
+    // range) take an out-of-range offset per lane.
     const uint32_t lds0 = lds_addr(lds_raw);
     auto issue = [&](int tile, int bufi) {
       const int key0 = tile * KT;
-      const int blk0 = key0 >> p.bs_log2;
-      const int in_blk = key0 & ((1 << p.bs_log2) - 1);      // nonzero only when block_size > KT
-      // The tile's block ids: every scalar load goes out before the first use
-      // (one round trip, not one per block).
-      int ids[NBLK];
+      int ids[GPW];
 #pragma unroll
-      for (int e = 0; e < NBLK; ++e) ids[e] = ld_uniform(p.bt + (int64_t)b * p.MB + min(blk0 + e, p.MB - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      u32x4_t rk[NBLK], rv[NBLK];
-#pragma unroll
-      for (int e = 0; e < NBLK; ++e) {
-        const int blk = clamp_block(ids[e], p.nblk);
-        const int first = e == 0 ? in_blk : 0;               // first row of the block in this tile
-        const int kfirst = ((blk0 + e) << p.bs_log2) + first;
-        const int nkeys = min(max(t.kv_hi - kfirst, 0), (1 << p.bs_log2) - first);
-        const int64_t row0 = ((int64_t)blk << p.bs_log2) + first;
-        rk[e] = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
-        if constexpr (SEP)
-          rv[e] = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int kg = key0 + 16 * (gi * NW + w);
+        ids[gi] = ld_uniform(p.bt + (int64_t)b * p.MB + min(kg >> p.bs_log2, p.MB - 1));
       }
-      const bool lower = key0 < t.kv_lo;
-      const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + w * 64 * 16);
+      __builtin_amdgcn_sched_barrier(0);   // every block-id load goes out before the first use
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
-        const int e = (((it * NW + w) * 64) / CPR) >> p.bs_log2;   // scalar: the slots' block
-        u32x4_t r = rk[0];
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int g = gi * NW + w;
+        const int kg = key0 + 16 * g;                     // first key of the group
+        const int nkeys = min(max(t.kv_hi - kg, 0), 16);
+        const int64_t row0 = ((int64_t)clamp_block(ids[gi], p.nblk) << p.bs_log2) + (kg & ((1 << p.bs_log2) - 1));
+        const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + g * 16 * CPR * 16);
+        const u32x4_t rk = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
+        const bool lower = kg < t.kv_lo;
 #pragma unroll
-        for (int q = 1; q < NBLK; ++q) r = (e == q) ? rk[q] : r;
-        uint32_t off = load_off[it];
-        if (lower) {
-          const int j = key0 + (it * NT + opaque_lane() + w * 64) / CPR;
-          off = j >= t.kv_lo ? off : kOutOfRange;
+        for (int i = 0; i < IPG; ++i) {
+          uint32_t off = load_off[i];
+          if (lower) off = kg + (i * 64 + opaque_lane()) / CPR >= t.kv_lo ? off : kOutOfRange;
+          copy16_to_lds(dst + i * 64 * 16, off, rk);
         }
-        copy16_to_lds(dst + it * NT * 16, off, r);
-      }
+        if constexpr (SEP) {
+          const uint32_t vdst = lds0 + (uint32_t)(bufi * BUF_BYTES + (TILE_CHUNKS + g * 16 * VCPR) * 16);
+          const u32x4_t rv = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
 #pragma unroll
-      for (int it = 0; it < VLOADS; ++it) {
-        const int e = (((it * NW + w) * 64) / VCPR) >> p.bs_log2;
-        u32x4_t r = rv[0];
-#pragma unroll
-        for (int q = 1; q < NBLK; ++q) r = (e == q) ? rv[q] : r;
-        uint32_t off = vload_off[it];
-        if (lower) {
-          const int j = key0 + (it * NT + opaque_lane() + w * 64) / VCPR;
-          off = j >= t.kv_lo ? off : kOutOfRange;
+          for (int i = 0; i < VIPG; ++i) {
+            uint32_t off = vload_off[i];
+            if (lower) off = kg + (i * 64 + opaque_lane()) / VCPR >= t.kv_lo ? off : kOutOfRange;
+            copy16_to_lds(vdst + i * 64 * 16, off, rv);
+          }
         }
-        copy16_to_lds(dst + (TILE_CHUNKS + it * NT) * 16, off, r);
       }
     };
 
@@ -699,8 +709,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       if (tt + NBUF - 1 < tile_b) issue(tt + NBUF - 1, (tt + NBUF - 1 - tile_a) % NBUF);
       if (wave_active) {
         const uint8_t* buf = lds_raw + bufi * BUF_BYTES;
+        const bool full = tt * KT >= lo_max_w && tt * KT + KT - 1 <= pos_min_w;
         tile_compute<DT, HSP, VHSP, KT, QREG, VCPR>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
-                                                    pos, lo_row, softcap_on, p);
+                                                    pos, lo_row, softcap_on, full, p);
       }
     }
     __syncthreads();
