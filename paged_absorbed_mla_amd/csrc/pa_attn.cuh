@@ -515,10 +515,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   constexpr int QSTRIDE = QREG + 8;     // staged rows padded by 16 bytes against bank conflicts
   constexpr int QRS = HSP - QREG + 8;
   constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
-  // Tile buffers: NBUF - 1 tiles are in flight while one is computed. Four
-  // waves get four buffers; a one-wave workgroup keeps two, so that several
-  // workgroups still fit in a CU's LDS.
-  constexpr int NBUF = 2;
+  // Tile buffers: NBUF - 1 tiles are in flight while one is computed. Three
+  // when two four-wave workgroups (two waves per SIMD) still fit in a CU's
+  // 160 KB of LDS, else two.
+  constexpr int NBUF = (NW >= 4 && 2 * 3 * BUF_BYTES <= 150 * 1024) ? 3 : 2;
   constexpr int PER = LOADS + VLOADS;   // copy instructions per wave and tile (vmcnt counts them)
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
   constexpr int KV_BYTES = (NBUF * BUF_BYTES > QSTAGE_BYTES) ? NBUF * BUF_BYTES : QSTAGE_BYTES;
@@ -597,45 +597,99 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
 
     WaveState<DT, HSP, VHSP, KT, QREG> st;
     // Query rows of this wave, staged through LDS (free between pieces),
-    // RoPE'd there with one thread per rotary pair, read back as fragments
-    // (row l32, channels 16 kk + 8 hi .. + 8).
+    // RoPE'd there, read back as fragments (row l32, channels 16 kk + 8 hi ..
+    // + 8). Every global load of a phase is issued before the first use of
+    // its result (a load-use loop would pay the memory latency per chunk).
     uint16_t* const qrest = (uint16_t*)(lds_raw + KV_BYTES) + w * 32 * QRS;
     {
       uint16_t* qs = (uint16_t*)lds_raw + w * 32 * QSTRIDE;
       // element (r, c) of this wave's staged query rows
       auto qel = [&](int r, int c) -> uint16_t* { return c < QREG ? qs + r * QSTRIDE + c : qrest + r * QRS + (c - QREG); };
       constexpr int QCH = HSP / 8;
-      for (int idx = lane; idx < 32 * QCH; idx += 64) {
+      constexpr int NQL = QCH / 2;     // 32 rows x QCH chunks over 64 lanes
+      u32x4_t qv[NQL];
+#pragma unroll
+      for (int q = 0; q < NQL; ++q) {
+        const int idx = q * 64 + lane;
         const int r = idx / QCH;
         const int c0 = (idx - r * QCH) * 8;
-        const int rl = w * 32 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (rl < t.nrows && c0 < p.hs) {
-          const int64_t gq = head_row(p, t, t.row0 + rl);
-          v = *(const u32x4_t*)(p.query + gq * p.hs + c0);
-        }
-        *(u32x4_t*)qel(r, c0) = v;
+        qv[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (w * 32 + r < t.nrows && c0 < p.hs)
+          qv[q] = *(const u32x4_t*)(p.query + head_row(p, t, t.row0 + w * 32 + r) * p.hs + c0);
+      }
+#pragma unroll
+      for (int q = 0; q < NQL; ++q) {
+        const int idx = q * 64 + lane;
+        const int r = idx / QCH;
+        *(u32x4_t*)qel(r, (idx - r * QCH) * 8) = qv[q];
       }
       __syncthreads();
       if (p.do_rotary) {
+        // One task rotates 8 channels of a row: non-interleaved, channels
+        // ro + 8 i .. + 8 with their partners half channels later (cos/sin
+        // entries 8 i .. + 8); interleaved, the 4 pairs of channels
+        // ro + 8 j .. + 8 (entries 4 j .. + 4). Tasks go four per lane at a
+        // time, table loads first.
         const int half = p.rd >> 1;
-        for (int idx = lane; idx < 32 * half; idx += 64) {
-          const int r = idx / half;
-          const int k = idx - r * half;
-          const int rl = w * 32 + r;
-          if (rl >= t.nrows) continue;
-          const int posr = past_b + (t.row0 + rl) / p.H;
-          const int d1 = p.interleaved ? p.ro + 2 * k : p.ro + k;
-          const int d2 = p.interleaved ? d1 + 1 : d1 + half;
-          const int64_t pr = min(max((int64_t)posr, (int64_t)0), p.prow - 1);
-          const float c = DT::to_f32(p.cos_t[pr * half + k]);
-          const float sn = DT::to_f32(p.sin_t[pr * half + k]);
-          uint16_t* e1 = qel(r, d1);
-          uint16_t* e2 = qel(r, d2);
-          const float x1 = DT::to_f32(*e1);
-          const float x2 = DT::to_f32(*e2);
-          *e1 = (uint16_t)DT::from_f32(x1 * c - x2 * sn);
-          *e2 = (uint16_t)DT::from_f32(x2 * c + x1 * sn);
+        const int per_row = p.interleaved ? p.rd / 8 : half / 8;
+        const int ntask = 32 * per_row;
+        for (int tb = 0; tb < ntask; tb += 4 * 64) {
+          u32x4_t cv[4], sv[4];
+          int rr[4], gg[4];
+          bool ok[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int task = tb + k * 64 + lane;
+            rr[k] = task / per_row;
+            gg[k] = task - rr[k] * per_row;
+            ok[k] = task < ntask && w * 32 + rr[k] < t.nrows;
+            cv[k] = sv[k] = u32x4_t{0u, 0u, 0u, 0u};
+            if (ok[k]) {
+              const int posr = past_b + (t.row0 + w * 32 + rr[k]) / p.H;
+              const int64_t e0 = min(max((int64_t)posr, (int64_t)0), p.prow - 1) * half;
+              if (p.interleaved) {
+                const u32x2_t c2 = *(const u32x2_t*)(p.cos_t + e0 + 4 * gg[k]);
+                const u32x2_t s2 = *(const u32x2_t*)(p.sin_t + e0 + 4 * gg[k]);
+                cv[k] = u32x4_t{c2[0], c2[1], 0u, 0u};
+                sv[k] = u32x4_t{s2[0], s2[1], 0u, 0u};
+              } else {
+                cv[k] = *(const u32x4_t*)(p.cos_t + e0 + 8 * gg[k]);
+                sv[k] = *(const u32x4_t*)(p.sin_t + e0 + 8 * gg[k]);
+              }
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (!ok[k]) continue;
+            float c[8], sn[8];
+            unpack8<DT>(cv[k], c);
+            unpack8<DT>(sv[k], sn);
+            if (p.interleaved) {
+              uint16_t* e = qel(rr[k], p.ro + 8 * gg[k]);
+              float x[8];
+              unpack8<DT>(*(const u32x4_t*)e, x);
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const float xe = x[2 * m], xo = x[2 * m + 1];
+                x[2 * m] = xe * c[m] - xo * sn[m];
+                x[2 * m + 1] = xo * c[m] + xe * sn[m];
+              }
+              *(u32x4_t*)e = pack8<DT>(x);
+            } else {
+              uint16_t* e1 = qel(rr[k], p.ro + 8 * gg[k]);
+              uint16_t* e2 = qel(rr[k], p.ro + 8 * gg[k] + half);
+              float x1[8], x2[8], y1[8], y2[8];
+              unpack8<DT>(*(const u32x4_t*)e1, x1);
+              unpack8<DT>(*(const u32x4_t*)e2, x2);
+#pragma unroll
+              for (int m = 0; m < 8; ++m) {
+                y1[m] = x1[m] * c[m] - x2[m] * sn[m];
+                y2[m] = x2[m] * c[m] + x1[m] * sn[m];
+              }
+              *(u32x4_t*)e1 = pack8<DT>(y1);
+              *(u32x4_t*)e2 = pack8<DT>(y2);
+            }
+          }
         }
       }
       __syncthreads();
