@@ -606,22 +606,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       // element (r, c) of this wave's staged query rows
       auto qel = [&](int r, int c) -> uint16_t* { return c < QREG ? qs + r * QSTRIDE + c : qrest + r * QRS + (c - QREG); };
       constexpr int QCH = HSP / 8;
+      // Lane-derived indices are formed here from an opaque lane id: hoisted
+      // out of the piece loop they would be kept in spill slots.
+      const int ln = opaque_lane();
       constexpr int NQL = QCH / 2;     // 32 rows x QCH chunks over 64 lanes
-      u32x4_t qv[NQL];
+      constexpr int QB = NQL > 8 ? (NQL + 1) / 2 : NQL;   // loads per batch (bounds the registers held)
 #pragma unroll
-      for (int q = 0; q < NQL; ++q) {
-        const int idx = q * 64 + lane;
-        const int r = idx / QCH;
-        const int c0 = (idx - r * QCH) * 8;
-        qv[q] = u32x4_t{0u, 0u, 0u, 0u};
-        if (w * 32 + r < t.nrows && c0 < p.hs)
-          qv[q] = *(const u32x4_t*)(p.query + head_row(p, t, t.row0 + w * 32 + r) * p.hs + c0);
-      }
+      for (int q0 = 0; q0 < NQL; q0 += QB) {
+        u32x4_t qv[QB];
 #pragma unroll
-      for (int q = 0; q < NQL; ++q) {
-        const int idx = q * 64 + lane;
-        const int r = idx / QCH;
-        *(u32x4_t*)qel(r, (idx - r * QCH) * 8) = qv[q];
+        for (int q = 0; q < QB; ++q) {
+          const int idx = (q0 + q) * 64 + ln;
+          const int r = idx / QCH;
+          const int c0 = (idx - r * QCH) * 8;
+          qv[q] = u32x4_t{0u, 0u, 0u, 0u};
+          if (q0 + q < NQL && w * 32 + r < t.nrows && c0 < p.hs)
+            qv[q] = *(const u32x4_t*)(p.query + head_row(p, t, t.row0 + w * 32 + r) * p.hs + c0);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int idx = (q0 + q) * 64 + ln;
+          const int r = idx / QCH;
+          if (q0 + q < NQL) *(u32x4_t*)qel(r, (idx - r * QCH) * 8) = qv[q];
+        }
       }
       __syncthreads();
       if (p.do_rotary) {
@@ -639,7 +646,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
           bool ok[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int task = tb + k * 64 + lane;
+            const int task = tb + k * 64 + ln;
             rr[k] = task / per_row;
             gg[k] = task - rr[k] * per_row;
             ok[k] = task < ntask && w * 32 + rr[k] < t.nrows;
