@@ -197,8 +197,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // The caller orders copies against LDS reads with explicit vmcnt waits and a
 // barrier. `rsrc` is a raw buffer descriptor (loads past its size read zeros).
 __device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, uint32_t voff, u32x4_t rsrc) {
+  // lds_base is wave-uniform by contract; readfirstlane keeps it in an SGPR
+  // where the compiler cannot prove that (the "s" constraint needs one).
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 // Raw buffer descriptor words over `bytes` bytes at `base` (stride 0, the same
@@ -377,23 +379,25 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     s[n / NKK] = DT::mfma32(cur, bq, s[n / NKK]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Scale (and softcap) into log2 units, mask, tile max. Lane holds keys
-  // hi*4 + (e&3) + 8*(e>>2) (+32 sub) of its row l32.
+  // Scores into log2 units, mask, tile max. Lane holds keys
+  // hi*4 + (e&3) + 8*(e>>2) (+32 sub) of its row l32. With a positive scale
+  // and no softcap the raw scores stay as they are: their max, times the
+  // scale, is the max of the scaled scores (rounding is monotone), and the
+  // scale is applied inside the exponent (one fma per score).
+  const bool raw = !softcap_on && p.scale_log2 > 0.0f;
   if (softcap_on) {
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[sub][e] = softcap_log2(s[sub][e], p.scale, p.softcap, p.softcap_inv);
-  } else {
+  } else if (!raw) {
+    const float sc = p.scale_log2;
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      // Element by element: a vector-times-scalar product would splat the
-      // scalar into 16 registers.
-      const float sc = p.scale_log2;
+    for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[sub][e] *= sc;
-    }
+      for (int e = 0; e < 16; ++e) s[sub][e] *= sc;   // element by element: a vector product would splat sc
   }
+  const float mul = raw ? p.scale_log2 : 1.0f;
   // `full` (wave-uniform): every row of the wave sees every key of the tile,
   // so no key is masked.
   float tmax = -INFINITY;
@@ -414,7 +418,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
       }
     }
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * mul;   // -inf stays -inf (mul > 0)
   // Lazy rescale: the reference max moves only when the tile max exceeds it by
   // more than 8 (log2 units), so probabilities stay <= 2^8, and the O
   // accumulators are rescaled only when some row of the wave moved it. The
@@ -426,7 +430,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   const bool rescale = bump && (st.m_run != -INFINITY);
   st.m_run = m_new;
   u32x4_t pf[NSUB][2];
-  float psum = 0.0f;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four partial sums: short dependency chains
 #pragma unroll
   for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
@@ -434,12 +438,13 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pv[e] = fast_exp2(s[sub][8 * k2 + e] - m_use);
-        psum += pv[e];
+        pv[e] = fast_exp2(__builtin_fmaf(s[sub][8 * k2 + e], mul, -m_use));
+        ps[e & 3] += pv[e];
       }
       pf[sub][k2] = pack8<DT>(pv);
     }
   }
+  const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
   st.l_run = st.l_run * corr + psum;
   if (__any(rescale)) {
 #pragma unroll
