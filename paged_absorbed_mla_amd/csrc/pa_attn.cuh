@@ -265,20 +265,23 @@ __device__ __forceinline__ float softcap_log2(float s, float scale, float cap, f
   return cap * th * kLog2e;
 }
 
-// Unit range handled by this workgroup. Workgroups are dispatched to the
-// eight XCDs (each with its own L2) round-robin by index, so when the grid is
-// a multiple of eight, XCD x takes the consecutive ranges x * grid/8 ..
-// (x + 1) * grid/8 - 1: ranges that share a query tile, and so read the same
-// query rows, then mostly share an L2.
-__device__ __forceinline__ int range_of_block() {
-  const int g = (int)gridDim.x, b = (int)blockIdx.x;
-  return (g & 7) == 0 ? (b & 7) * (g >> 3) + (b >> 3) : b;
-}
-
 // Scalar (s_load) read of data that no thread writes while the kernel runs:
 // block_table, sequence lengths and the schedule the previous launch wrote.
 __device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
   return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
+// Unit range handled by this workgroup. Workgroups are dispatched to the
+// eight XCDs (each with its own L2) round-robin by index, so when the grid is
+// a multiple of eight, XCD x takes the consecutive ranges x * grid/8 ..
+// (x + 1) * grid/8 - 1: ranges that share a query tile, and so read the same
+// query rows, then mostly share an L2. When the schedule uses fewer ranges
+// than workgroups (header[2], a short batch), range b goes to workgroup b,
+// so the ranges in use spread over every XCD.
+__device__ __forceinline__ int range_of_block(const int32_t* header) {
+  const int g = (int)gridDim.x, b = (int)blockIdx.x;
+  const int used = ld_uniform(header + 2);
+  return ((g & 7) == 0 && used >= g) ? (b & 7) * (g >> 3) + (b >> 3) : b;
 }
 
 // Block id clamped into [0, nblk): a block_table entry outside the cache (a
@@ -521,9 +524,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   constexpr int QRS = HSP - QREG + 8;
   constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
   // Tile buffers: NBUF - 1 tiles are in flight while one is computed. Three
-  // when two four-wave workgroups (two waves per SIMD) still fit in a CU's
-  // 160 KB of LDS, else two.
-  constexpr int NBUF = (NW >= 4 && 2 * 3 * BUF_BYTES <= 150 * 1024) ? 3 : 2;
+  // when two workgroups still fit in a CU's 160 KB of LDS, else two.
+  constexpr int NBUF = (2 * 3 * BUF_BYTES <= 150 * 1024) ? 3 : 2;
   constexpr int PER = LOADS + VLOADS;   // copy instructions per wave and tile (vmcnt counts them)
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
   constexpr int KV_BYTES = (NBUF * BUF_BYTES > QSTAGE_BYTES) ? NBUF * BUF_BYTES : QSTAGE_BYTES;
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int wr = range_of_block();
+  const int wr = range_of_block(p.header);
   int u = ld_uniform(p.wg_range + wr);
   const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;

@@ -23,6 +23,7 @@ struct SchedParams {
   int kvh;           // key/value heads: each sequence is scheduled once per head (H = query heads per head)
   int max_pos;       // max_blocks_per_seq * block_size: past lengths are clamped to it
   int piece_units;   // virtual KV tiles charged at the start of every query tile
+  int min_units;     // split-KV: fewest (virtual) units a workgroup's range may hold
   // Query pre-pass (blocks 1.., four-wave 576 kernel): the query with RoPE
   // applied, in the attention kernel's fragment order (qfrag, [T * H][hsp]).
   const uint16_t* query;
@@ -312,9 +313,13 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
 
   // D. Outputs: the tile table and the unit range and first tile of every
   // workgroup.
-  const int G = p.grid;
   const int64_t alpha = p.split_kv ? p.piece_units : 0;
   const int64_t Uv = U + alpha * M;
+  // Ranges used: all p.grid workgroups, or fewer when that would leave each
+  // fewer than min_units units (short batches: fewer, longer pieces, fewer
+  // partials to merge); the remaining workgroups get empty ranges.
+  const int G = p.split_kv ? (int)min((int64_t)p.grid, max((int64_t)1, (Uv + p.min_units - 1) / p.min_units))
+                           : p.grid;
   // 32-bit divisions when every product below fits (the usual case).
   const bool small = (Uv + alpha + 2) * (int64_t)G < ((int64_t)1 << 31);
   auto cut = [&](int w) -> int64_t {                   // x(w)
@@ -346,7 +351,7 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
       const int Pi = cnt(Vi + alpha + 1) - Wi;         // cuts inside the virtual prefix
       t.w_first = Wi + Pi - 1;
       t.npieces = Wn - t.w_first;
-      t.part_base = Pi > 0 ? t.w_first : G + i;        // slot of the first piece
+      t.part_base = Pi > 0 ? t.w_first : p.grid + i;   // slot of the first piece
       for (int w = Wi; w < Wn; ++w) {
         const int64_t o = cut(w) - Vi - alpha;
         p.wg_range[w] = u0[i] + (int32_t)min(max(o, (int64_t)0), (int64_t)(u0[i + 1] - u0[i]));
@@ -363,9 +368,9 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   }
   // Workgroups past the last cut inside a tile: empty ranges at the end.
   const int wtail = p.split_kv ? (M > 0 ? cnt(Uv) : 0) : M;
-  for (int w = wtail + (int)threadIdx.x; w <= G; w += kSchedThreads) {
+  for (int w = wtail + (int)threadIdx.x; w <= p.grid; w += kSchedThreads) {
     p.wg_range[w] = (int32_t)U;
-    if (w < G) p.wg_tile[w] = max(M - 1, 0);
+    if (w < p.grid) p.wg_tile[w] = max(M - 1, 0);
   }
   if (threadIdx.x == 0) {
     MTile t = {};
@@ -373,6 +378,7 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
     p.mt[M] = t;
     p.header[0] = (int32_t)U;
     p.header[1] = M;
+    p.header[2] = G;   // ranges in use (the rest are empty)
   }
 }
 
@@ -569,6 +575,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.wg_tile = (int32_t*)(wsb + ws.off_wg_tile);
   sp.sched = (int32_t*)(wsb + ws.off_sched);
   sp.piece_units = split_kv ? cfg.piece_units : 0;
+  sp.min_units = 4;
   sp.mt = (MTile*)(wsb + ws.off_mtiles);
   sp.query = (const uint16_t*)query;
   sp.cos_t = (const uint16_t*)cos_t;

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int wr = range_of_block();
+  const int wr = range_of_block(p.header);
   int u = ld_uniform(p.wg_range + wr);
   const int u_end = ld_uniform(p.wg_range + wr + 1);
   if (u >= u_end) return;
