@@ -548,24 +548,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   int i = ld_uniform(p.wg_tile + wr);   // query tile holding unit u
   const int i_first = i;
   const bool softcap_on = p.softcap > 0.0f;
-  // Copies move 16-key groups: group g of a tile (keys 16 g .. 16 g + 15)
-  // lies in one cache block (block_size >= 16 and a power of two), so one
-  // descriptor serves all its copy instructions; wave w copies groups
-  // w, w + NW, ... Copy instruction i of a group fills LDS slots
+  // Copies move groups of GK keys: group g of a tile (keys GK g .. GK g +
+  // GK - 1) lies in one cache block (block_size >= 16, a power of two, and GK
+  // divides 16), so one descriptor serves all its copy instructions; wave w
+  // copies groups w, w + NW, ... Copy instruction i of a group fills LDS slots
   // 64 i .. 64 i + 63 of the group's rows. load_off[i]: byte offset, from the
   // group's first row, of the chunk the lane copies (chunks past the head, for
   // padded head sizes, get an offset past every descriptor and land as zeros).
-  constexpr int KG = KT / 16;           // key groups per tile
+  constexpr int GK = (KT / NW) < 16 ? (KT / NW) : 16;   // keys per copy group
+  constexpr int KG = KT / GK;           // key groups per tile
   constexpr int GPW = KG / NW;          // groups per wave
-  constexpr int IPG = CPR / 4;          // K copy instructions per group (16 rows x CPR chunks / 64)
-  constexpr int VIPG = SEP ? VCPR / 4 : 0;
-  static_assert(KG % NW == 0 && CPR % 4 == 0 && GPW * IPG == LOADS && GPW * VIPG == VLOADS, "copy split");
+  constexpr int IPG = GK * CPR / 64;    // K copy instructions per group
+  constexpr int VIPG = SEP ? GK * VCPR / 64 : 0;
+  static_assert(KG % NW == 0 && (GK * CPR) % 64 == 0 && (GK * VCPR) % 64 == 0 && GPW * IPG == LOADS &&
+                GPW * VIPG == VLOADS, "copy split");
+  // The LDS swizzle follows the key index within the tile (period 16); with
+  // one group per wave that is GK w + kl, else (GK = 16) kl.
+  const int swz0 = GPW == 1 ? GK * w : 0;
   uint32_t load_off[IPG];
 #pragma unroll
   for (int i = 0; i < IPG; ++i) {
     const int pidx = i * 64 + lane;
     const int kl = pidx / CPR;
-    const int lc = (pidx - kl * CPR) ^ lds_swizzle(kl);
+    const int lc = (pidx - kl * CPR) ^ lds_swizzle(swz0 + kl);
     load_off[i] = lc * 8 < p.hs ? (uint32_t)((kl * p.krs + lc * 8) * 2) : kOutOfRange;
   }
   uint32_t vload_off[VIPG > 0 ? VIPG : 1];
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   for (int i = 0; i < VIPG; ++i) {
     const int pidx = i * 64 + lane;
     const int kl = pidx / VCPR;
-    const int lc = (pidx - kl * VCPR) ^ lds_swizzle(kl);
+    const int lc = (pidx - kl * VCPR) ^ lds_swizzle(swz0 + kl);
     vload_off[i] = lc * 8 < p.vhs ? (uint32_t)((kl * p.vrs + lc * 8) * 2) : kOutOfRange;
   }
 
@@ -728,17 +733,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       int ids[GPW];
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi) {
-        const int kg = key0 + 16 * (gi * NW + w);
+        const int kg = key0 + GK * (gi * NW + w);
         ids[gi] = ld_uniform(p.bt + (int64_t)b * p.MB + min(kg >> p.bs_log2, p.MB - 1));
       }
       __builtin_amdgcn_sched_barrier(0);   // every block-id load goes out before the first use
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi) {
         const int g = gi * NW + w;
-        const int kg = key0 + 16 * g;                     // first key of the group
-        const int nkeys = min(max(t.kv_hi - kg, 0), 16);
+        const int kg = key0 + GK * g;                     // first key of the group
+        const int nkeys = min(max(t.kv_hi - kg, 0), GK);
         const int64_t row0 = ((int64_t)clamp_block(ids[gi], p.nblk) << p.bs_log2) + (kg & ((1 << p.bs_log2) - 1));
-        const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + g * 16 * CPR * 16);
+        const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + g * GK * CPR * 16);
         const u32x4_t rk = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
         const bool lower = kg < t.kv_lo;
 #pragma unroll
@@ -748,7 +753,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
           copy16_to_lds(dst + i * 64 * 16, off, rk);
         }
         if constexpr (SEP) {
-          const uint32_t vdst = lds0 + (uint32_t)(bufi * BUF_BYTES + (TILE_CHUNKS + g * 16 * VCPR) * 16);
+          const uint32_t vdst = lds0 + (uint32_t)(bufi * BUF_BYTES + (TILE_CHUNKS + g * GK * VCPR) * 16);
           const u32x4_t rv = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
 #pragma unroll
           for (int i = 0; i < VIPG; ++i) {

@@ -192,6 +192,9 @@ EDGES = {
     "hs80_padded": dict(head_size=80, v_head_size=48, rotary_offset=16, rotary_dim=64),
     "glm_dims_128heads": dict(num_heads=128, head_size=192, v_head_size=128, rotary_dim=64,
                               rotary_offset=128, block_size=64, past=[100, 700], new=[1, 1]),
+    # long bfloat16 prefill on GLM dims (four-wave instance, two workgroups per CU)
+    "glm_dims_prefill_bf16": dict(num_heads=16, head_size=192, v_head_size=128, rotary_dim=64,
+                                  rotary_offset=128, block_size=16, past=[0, 300], new=[200, 150]),
     "dsv3_dims_multi_token": dict(num_heads=16, head_size=576, v_head_size=512, rotary_dim=64,
                                   rotary_offset=512, block_size=16, past=[33, 0], new=[9, 17]),
     "empty_middle_seq": dict(past=[4, 50, 7], new=[3, 0, 5]),

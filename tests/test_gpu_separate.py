@@ -94,6 +94,9 @@ EDGES = {
     "bf16_decode_64_wide": dict(dtype="bf16", past=[900, 17, 2500], new=[1, 1, 1], head_size=64,
                                 v_head_size=64, rotary_dim=32, scale=0.0, has_scale=0),
     "empty_middle_seq": dict(past=[4, 50, 7], new=[3, 0, 5]),
+    # longer prefill chunks, both storage types
+    "prefill_f16": dict(past=[0, 300], new=[200, 150], num_heads=32, kv_num_heads=8),
+    "prefill_bf16": dict(dtype="bf16", past=[0, 300], new=[200, 150], num_heads=32, kv_num_heads=8),
 }
 
 
