@@ -868,36 +868,45 @@ __device__ __forceinline__ int64_t piece_slot(const MTile& t, int q) {
 // domain) and denominator l_i; with
 // M = max_i m_i and c_i = 2^(m_i - M) l_i, out = sum_i c_i o_i / sum_i c_i
 // (float32), rounded to nearest even.
-// Grid: (query tiles, RW / kCombineRows) of 256 threads. TPR threads share a
-// row; thread j of a row owns the 8-channel groups j, j + TPR, j + 2 TPR, ...
-// (so each load instruction covers contiguous bytes of a row). Every thread
-// forms its row's weights itself from the (m, l) pairs. Up to QA pieces: the
-// pairs and all slice loads go out together (one round trip). More pieces:
-// the pairs are read 8 pieces at a time, then the slices 4 pieces at a time
-// with all their 16-byte loads in flight together.
-constexpr int kCombineRows = 16;
+// Grid: (query tiles, ceil(RW / ROWS)) of 256 threads, ROWS rows per block.
+// TPR threads share a row; thread j of a row owns the 8-channel groups j,
+// j + TPR, j + 2 TPR, ... (so each load instruction covers contiguous bytes
+// of a row). Every thread forms its row's weights itself from the (m, l)
+// pairs. Up to QA pieces: the pairs and all slice loads go out together (one
+// round trip). More pieces: the pairs are read QM pieces at a time, then the
+// slices QA pieces at a time with all their 16-byte loads in flight together.
+template <int VHSP>
+struct CombineShape {
+  static constexpr int TPR = (VHSP / 8) < 32 ? (VHSP / 8) : 32;   // threads per row
+  static constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 8)
+  static constexpr int ROWS = 256 / TPR;                          // rows per block
+  static constexpr int NV = CPT / 8;
+  static constexpr int QA = NV <= 2 ? 8 : 4;                      // pieces per round trip
+};
 
 template <typename DT, int VHSP, int RW>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  constexpr int TPR = (VHSP / 8) < 16 ? (VHSP / 8) : 16;   // threads per row
-  constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 8)
-  constexpr int ROWS = 256 / TPR;                          // rows per pass
-  constexpr int NV = CPT / 8;
+  using CS = CombineShape<VHSP>;
+  constexpr int TPR = CS::TPR;
+  constexpr int CPT = CS::CPT;
+  constexpr int ROWS = CS::ROWS;
+  constexpr int NV = CS::NV;
   constexpr int QM = 8;                                    // pieces per batch of (m, l) loads
-  constexpr int QA = 4;                                    // pieces per batch of slice loads
+  constexpr int QA = CS::QA;                               // pieces per batch of slice loads
   static_assert(CPT % 8 == 0 && CPT * TPR == VHSP, "channel split");
   const int i = blockIdx.x;
   if (i >= ld_uniform(p.header + 1)) return;
   const MTile t = ld_uniform_tile(p.mt + i);
   if (t.npieces <= 1) return;
-  const int r0 = blockIdx.y * kCombineRows;
+  const int r0 = blockIdx.y * ROWS;
   if (r0 >= t.nrows) return;
   const int nq = t.npieces;
-  for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += ROWS) {
+  {
+    const int rr = threadIdx.x / TPR;
     const int r = r0 + rr;
-    if (r >= t.nrows) continue;
+    if (r >= t.nrows) return;
     const int c0 = (threadIdx.x % TPR) * 8;                 // channel of group 0; group v at c0 + 8 TPR v
-    if (c0 >= p.vhs) continue;
+    if (c0 >= p.vhs) return;
     // Piece q's (m, l) and slice (16-byte aligned: row and slot strides are
     // multiples of 16 bytes).
     auto ml_of = [&](int q) -> const float* { return p.part_ml + (piece_slot(t, q) * RW + r) * 2; };
@@ -920,12 +929,19 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       float m[QA], l[QA];
 #pragma unroll
       for (int k = 0; k < QA; ++k) {
-        const bool ok = k < nq;
-        const int q = ok ? k : 0;
-        m[k] = ok ? ml_of(q)[0] : -INFINITY;
-        l[k] = ok ? ml_of(q)[1] : 0.0f;
+        // Pieces past nq (uniform over the block) load nothing.
+        m[k] = -INFINITY;
+        l[k] = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po_of(q) + 8 * TPR * v, a[k][v]);
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[k][v][e] = 0.0f;
+        if (k < nq) {
+          m[k] = ml_of(k)[0];
+          l[k] = ml_of(k)[1];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) load_part8<DT>(p.part_o, po_of(k) + 8 * TPR * v, a[k][v]);
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -1018,7 +1034,8 @@ typedef hipError_t (*AttnOccFn)(int*);
     e = hipGetLastError();                                                                                \
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                              \
     if (e != hipSuccess || !combine) return e;                                                            \
-    combine_kernel<DT, VHSP, NW * 32><<<dim3(cgrid, (NW * 32) / kCombineRows), 256, 0, s>>>(p);           \
+    combine_kernel<DT, VHSP, NW * 32>                                                                     \
+        <<<dim3(cgrid, (NW * 32 + CombineShape<VHSP>::ROWS - 1) / CombineShape<VHSP>::ROWS), 256, 0, s>>>(p);     \
     return hipGetLastError();                                                                             \
   }                                                                                                       \
   }

@@ -877,7 +877,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     e = hipGetLastError();                                                                              \
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                            \
     if (e != hipSuccess || !combine) return e;                                                          \
-    combine_kernel<DT, VHSP, 128><<<dim3(cgrid, 128 / kCombineRows), 256, 0, s>>>(p);                   \
+    combine_kernel<DT, VHSP, 128><<<dim3(cgrid, 128 / CombineShape<VHSP>::ROWS), 256, 0, s>>>(p);        \
     return hipGetLastError();                                                                           \
   }                                                                                                     \
   }
