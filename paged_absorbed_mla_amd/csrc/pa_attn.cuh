@@ -74,7 +74,7 @@ struct AttnParams {
   const uint16_t* sin_t;
   const int32_t* bt;
   uint16_t* out;
-  const int32_t* header;    // [0] work units U, [1] query tiles M
+  const int32_t* header;    // [0] work units U, [1] query tiles M, [2] unit ranges in use
   const int32_t* wg_range;  // [grid + 1] unit range of each workgroup
   const int32_t* wg_tile;   // [grid] query tile holding each workgroup's first unit
   const MTile* mt;          // [M + 1], mt[M].unit0 = U
