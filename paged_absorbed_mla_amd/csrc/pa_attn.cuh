@@ -780,9 +780,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       vm_wait_tiles<PER, NBUF - 2>(min(NBUF - 2, tile_b - 1 - tt));
       lds_barrier();
       if (tt + NBUF - 1 < tile_b) issue(tt + NBUF - 1, (tt + NBUF - 1 - tile_a) % NBUF);
-      if (wave_active) {
+      {
+        // Every wave computes, also one without rows in this tile (its rows
+        // are zero queries and are never stored): a branch here would make
+        // the accumulators loop-carried through two paths, and the compiler
+        // then copies them at every iteration.
         const uint8_t* buf = lds_raw + bufi * BUF_BYTES;
-        const bool full = tt * KT >= lo_max_w && tt * KT + KT - 1 <= pos_min_w;
+        const bool full = wave_active && tt * KT >= lo_max_w && tt * KT + KT - 1 <= pos_min_w;
         tile_compute<DT, HSP, VHSP, KT, QREG, VCPR>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
                                                     pos, lo_row, softcap_on, full, p);
       }
