@@ -85,6 +85,7 @@ struct AttnParams {
   const uint16_t* qfrag;    // [T * H][HSP]: RoPE'd query in fragment order (four-wave 576 kernel)
   const uint16_t* vcache;   // separate layout: value cache [slots][kvh][vhs] (null in the latent layout)
   int nblk;                 // num_blocks (< 2^31 / block_size): block ids are clamped into [0, nblk)
+  int kv_stream;            // 1: every KV row is read by one query tile only (a decode-shaped call)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H;                    // query heads per key/value head (rows per token of a query tile)
   int Hq;                   // query heads of the call (H * kvh): head stride of query and output rows
@@ -196,11 +197,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // otherwise drain every in-flight copy (vmcnt(0)) before the next LDS read.
 // The caller orders copies against LDS reads with explicit vmcnt waits and a
 // barrier. `rsrc` is a raw buffer descriptor (loads past its size read zeros).
+// NT: non-temporal (streaming) cache policy, for data that no other
+// workgroup reads again within the launch (a decode step's KV rows): such
+// copies stream from HBM faster with it. Data that other query tiles re-read
+// (prefill) keeps the default policy, which leaves it in L2 for them.
+template <bool NT = false>
 __device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, uint32_t voff, u32x4_t rsrc) {
   // lds_base is wave-uniform by contract; readfirstlane keeps it in an SGPR
   // where the compiler cannot prove that (the "s" constraint needs one).
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 // Raw buffer descriptor words over `bytes` bytes at `base` (stride 0, the same

@@ -614,10 +614,14 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   ap.part_slot = ws.part_slot;
   ap.part_row = ws.part_row;
   ap.qfrag = sp.qfrag;
+  ap.H = g.H / g.kvh;
   ap.nblk = (int)g.NB;   // NB * block_size <= INT32_MAX (checked by the entry points)
+  // Decode-shaped call (no more tokens than sequences, a token's heads within one
+  // query tile): each KV row is read by one query tile only, so the four-wave
+  // 576/512 kernel's copies take the streaming cache policy.
+  ap.kv_stream = (g.T <= g.B && ap.H <= cfg.rows()) ? 1 : 0;
   ap.prow = g.do_rotary ? g.P : 1;
   ap.vcache = (const uint16_t*)value_cache;
-  ap.H = g.H / g.kvh;
   ap.Hq = g.H;
   ap.krs = g.kvh * g.hs;
   ap.vrs = g.kvh * g.vhs;

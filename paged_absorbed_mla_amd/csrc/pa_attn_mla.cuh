@@ -423,7 +423,9 @@ __device__ __forceinline__ void mla_pv(MlaState<HSP, VHSP>& st, uint32_t Lv, con
   });
 }
 
-template <typename DT, int HSP, int VHSP>
+// NT: the tile copies take the streaming cache policy (launched for
+// decode-shaped calls, where no other query tile re-reads a KV row).
+template <typename DT, int HSP, int VHSP, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mla_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4;
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int j = c.kw0 + (it * 64 + opaque_lane()) / CPR;
         off = j >= t.kv_lo ? off : kOutOfRange;
       }
-      copy16_to_lds(c.dst0 + it * 64 * 16, off, c.rsrc);
+      copy16_to_lds<NT>(c.dst0 + it * 64 * 16, off, c.rsrc);
     };
     auto issue = [&](int tile, int bufi, int blk_raw) {
       const CopyPlan c = plan(tile, bufi, blk_raw);
@@ -866,14 +868,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #define PA_DEFINE_ATTN_MLA_INSTANCE(DT, DTN, HSP, VHSP)                                                 \
   namespace pa {                                                                                        \
   hipError_t PA_ATTN_FN(lat, DTN, HSP, VHSP, 4, 32, occ)(int* n) {                                           \
-    void (*fn)(AttnParams) = attn_mla_kernel<DT, HSP, VHSP>;                                            \
+    void (*fn)(AttnParams) = attn_mla_kernel<DT, HSP, VHSP, true>;                                      \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), 256, 0);  \
   }                                                                                                     \
   hipError_t PA_ATTN_FN(lat, DTN, HSP, VHSP, 4, 32, launch)(const AttnParams& p, int grid, bool combine,      \
                                                        int cgrid, hipStream_t s, const hipEvent_t* ev) { \
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                          \
     if (e != hipSuccess) return e;                                                                      \
-    attn_mla_kernel<DT, HSP, VHSP><<<grid, 256, 0, s>>>(p);                                             \
+    if (p.kv_stream) attn_mla_kernel<DT, HSP, VHSP, true><<<grid, 256, 0, s>>>(p);                      \
+    else attn_mla_kernel<DT, HSP, VHSP, false><<<grid, 256, 0, s>>>(p);                                 \
     e = hipGetLastError();                                                                              \
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                            \
     if (e != hipSuccess || !combine) return e;                                                          \

@@ -5,6 +5,7 @@ writes a source of an inline-assembly MFMA without wait states in between
 the kernel's device assembly with the library's own flags (hipcc
 cross-compiles gfx950 without a GPU)."""
 import os
+import re
 import subprocess
 import tempfile
 
@@ -31,10 +32,14 @@ def _device_asm(src):
         return open(out).read()
 
 
+@pytest.mark.parametrize("nt", [0, 1])
 @pytest.mark.parametrize("inst", ["attnm_bf16_576_512.hip", "attnm_f16_576_512.hip"])
-def test_mla_kernel_lds_reads_are_waited_for(inst):
+def test_mla_kernel_lds_reads_are_waited_for(inst, nt):
+    """Both copy-policy variants of the 576/512 kernel (template flag NT)."""
     asm = _device_asm(os.path.join(ROOT, "paged_absorbed_mla_amd", "csrc", "inst", inst))
-    lines = kernel_lines(asm, "_ZN2pa15attn_mla_kernel")
+    syms = re.findall(r"^(_ZN2pa15attn_mla_kernel\S*?Lb%dE\S*):" % nt, asm, re.M)
+    assert syms, "kernel symbol not found"
+    lines = kernel_lines(asm, syms[0])
     assert len(lines) > 1000, "kernel body not found"
     found = check(lines)
     assert not found, "\n".join(f"line {a}: {b} uses {c} of the LDS read at line {d}" for a, b, c, d in found[:10])
