@@ -529,7 +529,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   static_assert(!SEP || VHSP % 64 == 0, "value rows: whole swizzle periods");
   static_assert(QREG % 16 == 0 && QREG <= HSP, "register part of the query");
   // LDS: [KV tile buffers | persistent query rows, channels >= QREG]. Before the
-  // tile loop the buffer region stages the register part of the query.
+  // tile loop the buffer region (EARLY below: its last buffer) stages the
+  // register part of the query.
   constexpr int QSTRIDE = QREG + 8;     // staged rows padded by 16 bytes against bank conflicts
   constexpr int QRS = HSP - QREG + 8;
   constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
@@ -538,6 +539,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   constexpr int NBUF = (2 * 3 * BUF_BYTES <= 150 * 1024) ? 3 : 2;
   constexpr int PER = LOADS + VLOADS;   // copy instructions per wave and tile (vmcnt counts them)
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
+  // When the staged query fits in one tile buffer it is staged in the last
+  // one, and the first NBUF - 1 tiles of a piece are issued before the query
+  // loads (into the other buffers), so the two latencies overlap (the
+  // one-wave decode instances).
+  constexpr bool EARLY = QSTAGE_BYTES <= BUF_BYTES;
+  constexpr int QSTAGE_OFF = EARLY ? (NBUF - 1) * BUF_BYTES : 0;
   constexpr int KV_BYTES = (NBUF * BUF_BYTES > QSTAGE_BYTES) ? NBUF * BUF_BYTES : QSTAGE_BYTES;
   constexpr int QREST_BYTES = (QREG < HSP) ? RW * QRS * 2 : 0;
   constexpr int LDS_BYTES = KV_BYTES + QREST_BYTES;
@@ -617,6 +624,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     const int lo_max_w = p.window >= 0 ? max(0, pos_max_w - p.window) : 0;
     const int64_t qrow = head_row(p, t, R);
 
+    // Copy KV tile `tile` into LDS buffer `bufi`: exactly PER copy
+    // instructions per wave (vmcnt counts them), 16 bytes per lane, global ->
+    // LDS directly. A group's descriptor covers its keys below kv_hi, so later
+    // keys land as zeros; keys below kv_lo (the first tile of a windowed
+    // range) take an out-of-range offset per lane.
+    const uint32_t lds0 = lds_addr(lds_raw);
+    auto issue = [&](int tile, int bufi) {
+      const int key0 = tile * KT;
+      int ids[GPW];
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int kg = key0 + GK * (gi * NW + w);
+        ids[gi] = ld_uniform(p.bt + (int64_t)b * p.MB + min(kg >> p.bs_log2, p.MB - 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // every block-id load goes out before the first use
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int g = gi * NW + w;
+        const int kg = key0 + GK * g;                     // first key of the group
+        const int nkeys = min(max(t.kv_hi - kg, 0), GK);
+        const int64_t row0 = ((int64_t)clamp_block(ids[gi], p.nblk) << p.bs_log2) + (kg & ((1 << p.bs_log2) - 1));
+        const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + g * GK * CPR * 16);
+        const u32x4_t rk = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
+        const bool lower = kg < t.kv_lo;
+#pragma unroll
+        for (int i = 0; i < IPG; ++i) {
+          uint32_t off = load_off[i];
+          if (lower) off = kg + (i * 64 + opaque_lane()) / CPR >= t.kv_lo ? off : kOutOfRange;
+          copy16_to_lds(dst + i * 64 * 16, off, rk);
+        }
+        if constexpr (SEP) {
+          const uint32_t vdst = lds0 + (uint32_t)(bufi * BUF_BYTES + (TILE_CHUNKS + g * GK * VCPR) * 16);
+          const u32x4_t rv = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
+#pragma unroll
+          for (int i = 0; i < VIPG; ++i) {
+            uint32_t off = vload_off[i];
+            if (lower) off = kg + (i * 64 + opaque_lane()) / VCPR >= t.kv_lo ? off : kOutOfRange;
+            copy16_to_lds(vdst + i * 64 * 16, off, rv);
+          }
+        }
+      }
+    };
+
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k)
+        if (tile_a + k < tile_b) issue(tile_a + k, k);
+    }
     WaveState<DT, HSP, VHSP, KT, QREG> st;
     // Query rows of this wave, staged through LDS (free between pieces),
     // RoPE'd there, read back as fragments (row l32, channels 16 kk + 8 hi ..
@@ -624,7 +679,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     // its result (a load-use loop would pay the memory latency per chunk).
     uint16_t* const qrest = (uint16_t*)(lds_raw + KV_BYTES) + w * 32 * QRS;
     {
-      uint16_t* qs = (uint16_t*)lds_raw + w * 32 * QSTRIDE;
+      uint16_t* qs = (uint16_t*)(lds_raw + QSTAGE_OFF) + w * 32 * QSTRIDE;
       // element (r, c) of this wave's staged query rows
       auto qel = [&](int r, int c) -> uint16_t* { return c < QREG ? qs + r * QSTRIDE + c : qrest + r * QRS + (c - QREG); };
       constexpr int QCH = HSP / 8;
@@ -732,56 +787,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     st.m_run = -INFINITY;
     st.l_run = 0.0f;
 
-    // Copy KV tile `tile` into LDS buffer `bufi`: exactly PER copy
-    // instructions per wave (vmcnt counts them), 16 bytes per lane, global ->
-    // LDS directly. A group's descriptor covers its keys below kv_hi, so later
-    // keys land as zeros; keys below kv_lo (the first tile of a windowed
-    // range) take an out-of-range offset per lane.
-    const uint32_t lds0 = lds_addr(lds_raw);
-    auto issue = [&](int tile, int bufi) {
-      const int key0 = tile * KT;
-      int ids[GPW];
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        const int kg = key0 + GK * (gi * NW + w);
-        ids[gi] = ld_uniform(p.bt + (int64_t)b * p.MB + min(kg >> p.bs_log2, p.MB - 1));
-      }
-      __builtin_amdgcn_sched_barrier(0);   // every block-id load goes out before the first use
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        const int g = gi * NW + w;
-        const int kg = key0 + GK * g;                     // first key of the group
-        const int nkeys = min(max(t.kv_hi - kg, 0), GK);
-        const int64_t row0 = ((int64_t)clamp_block(ids[gi], p.nblk) << p.bs_log2) + (kg & ((1 << p.bs_log2) - 1));
-        const uint32_t dst = lds0 + (uint32_t)(bufi * BUF_BYTES + g * GK * CPR * 16);
-        const u32x4_t rk = rsrc_words_u(p.cache + row0 * p.krs + t.kvg * p.hs, (uint32_t)(nkeys * p.krs * 2));
-        const bool lower = kg < t.kv_lo;
-#pragma unroll
-        for (int i = 0; i < IPG; ++i) {
-          uint32_t off = load_off[i];
-          if (lower) off = kg + (i * 64 + opaque_lane()) / CPR >= t.kv_lo ? off : kOutOfRange;
-          copy16_to_lds(dst + i * 64 * 16, off, rk);
-        }
-        if constexpr (SEP) {
-          const uint32_t vdst = lds0 + (uint32_t)(bufi * BUF_BYTES + (TILE_CHUNKS + g * GK * VCPR) * 16);
-          const u32x4_t rv = rsrc_words_u(p.vcache + row0 * p.vrs + t.kvg * p.vhs, (uint32_t)(nkeys * p.vrs * 2));
-#pragma unroll
-          for (int i = 0; i < VIPG; ++i) {
-            uint32_t off = vload_off[i];
-            if (lower) off = kg + (i * 64 + opaque_lane()) / VCPR >= t.kv_lo ? off : kOutOfRange;
-            copy16_to_lds(vdst + i * 64 * 16, off, rv);
-          }
-        }
-      }
-    };
-
     // Ring of NBUF buffers: tile tt sits in buffer (tt - tile_a) % NBUF; the
-    // first NBUF - 1 tiles go out before the loop, and iteration tt, once every
-    // wave has passed its barrier (so the buffer of tile tt - 1 is free),
-    // issues tile tt + NBUF - 1 into that buffer.
+    // first NBUF - 1 tiles go out before the loop (EARLY: before the query
+    // staging), and iteration tt, once every wave has passed its barrier (so
+    // the buffer of tile tt - 1 is free), issues tile tt + NBUF - 1 into that
+    // buffer.
+    if constexpr (!EARLY) {
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-      if (tile_a + k < tile_b) issue(tile_a + k, k);
+      for (int k = 0; k < NBUF - 1; ++k)
+        if (tile_a + k < tile_b) issue(tile_a + k, k);
+    }
     for (int tt = tile_a; tt < tile_b; ++tt) {
       const int bufi = (tt - tile_a) % NBUF;
       // This wave's copies of tile tt are done once at most (tiles issued

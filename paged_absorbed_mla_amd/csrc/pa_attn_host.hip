@@ -465,6 +465,13 @@ static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
   return nullptr;
 }
 
+// Scheduling charge of a piece of the generic kernel, in KV tiles: the query
+// staging and the epilogue take about three 64-key tiles' time on the
+// four-wave (prefill) instances, where a workgroup often holds several short
+// pieces; the one-wave decode pieces are long and their staging overlaps the
+// first tile copies.
+static int generic_piece_units(int nw) { return nw >= 4 ? 4 : 2; }
+
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
   cfg->wide = 0;
@@ -478,6 +485,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
     else return false;
     cfg->nw = rows_per_seq >= 96 ? 4 : 1;
     cfg->kt = (cfg->hsp == 64 && cfg->nw == 1) ? 32 : 64;
+    cfg->piece_units = generic_piece_units(cfg->nw);
     return find_instance(g.dtype, *cfg) != nullptr;
   }
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
@@ -485,7 +493,10 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 10; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
-  if (!cfg->wide) cfg->nw = rows_per_seq >= 96 ? 4 : 1;
+  if (!cfg->wide) {
+    cfg->nw = rows_per_seq >= 96 ? 4 : 1;
+    cfg->piece_units = generic_piece_units(cfg->nw);
+  }
   if (cfg->hsp == 64 && cfg->nw == 4) cfg->kt = 64;   // staged query rows need 2 tiles >= 32 * nw rows
   return find_instance(g.dtype, *cfg) != nullptr;
 }
