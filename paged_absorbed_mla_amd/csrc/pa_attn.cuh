@@ -802,6 +802,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       // This wave's copies of tile tt are done once at most (tiles issued
       // after it) * PER copies remain in flight; the barrier then makes every
       // wave's copies of tile tt visible.
+      if constexpr (NW >= 4) {
+        // Two workgroups share a CU (one wave of each per SIMD). With equal
+        // priorities the SIMDs favour the older wave, so the workgroups of
+        // the grid's first half ran ahead and those of the second half
+        // finished last; the priority alternates every tile, in opposite
+        // phase in the two halves, so both share the SIMDs evenly.
+        if (((tt & 1) != 0) != (blockIdx.x >= gridDim.x / 2)) asm volatile("s_setprio 1");
+        else asm volatile("s_setprio 0");
+      }
       vm_wait_tiles<PER, NBUF - 2>(min(NBUF - 2, tile_b - 1 - tt));
       lds_barrier();
       if (tt + NBUF - 1 < tile_b) issue(tt + NBUF - 1, (tt + NBUF - 1 - tile_a) % NBUF);
