@@ -686,93 +686,97 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       // Lane-derived indices are formed here from an opaque lane id: hoisted
       // out of the piece loop they would be kept in spill slots.
       const int ln = opaque_lane();
-      constexpr int NQL = QCH / 2;     // 32 rows x QCH chunks over 64 lanes
-      constexpr int QB = NQL > 8 ? (NQL + 1) / 2 : NQL;   // loads per batch (bounds the registers held)
+      // RoPE: one task rotates 8 channels of a row: non-interleaved, channels
+      // ro + 8 i .. + 8 with their partners half channels later (cos/sin
+      // entries 8 i .. + 8); interleaved, the 4 pairs of channels
+      // ro + 8 j .. + 8 (entries 4 j .. + 4). Tasks go four per lane at a
+      // time. The table entries of the first four tasks are loaded together
+      // with the query rows (they depend only on the rows' positions), so
+      // the staging waits for memory once.
+      const int half = p.rd >> 1;
+      const int per_row = p.interleaved ? p.rd / 8 : half / 8;
+      const int ntask = p.do_rotary ? 32 * per_row : 0;
+      u32x4_t cv[4], sv[4];
+      int rr[4], gg[4];
+      bool ok[4];
+      auto load_tables = [&](int tb) {
 #pragma unroll
-      for (int q0 = 0; q0 < NQL; q0 += QB) {
-        u32x4_t qv[QB];
+        for (int k = 0; k < 4; ++k) {
+          const int task = tb + k * 64 + ln;
+          rr[k] = task / per_row;
+          gg[k] = task - rr[k] * per_row;
+          ok[k] = task < ntask && w * 32 + rr[k] < t.nrows;
+          cv[k] = sv[k] = u32x4_t{0u, 0u, 0u, 0u};
+          if (ok[k]) {
+            const int posr = past_b + (t.row0 + w * 32 + rr[k]) / p.H;
+            const int64_t e0 = min(max((int64_t)posr, (int64_t)0), p.prow - 1) * half;
+            if (p.interleaved) {
+              const u32x2_t c2 = *(const u32x2_t*)(p.cos_t + e0 + 4 * gg[k]);
+              const u32x2_t s2 = *(const u32x2_t*)(p.sin_t + e0 + 4 * gg[k]);
+              cv[k] = u32x4_t{c2[0], c2[1], 0u, 0u};
+              sv[k] = u32x4_t{s2[0], s2[1], 0u, 0u};
+            } else {
+              cv[k] = *(const u32x4_t*)(p.cos_t + e0 + 8 * gg[k]);
+              sv[k] = *(const u32x4_t*)(p.sin_t + e0 + 8 * gg[k]);
+            }
+          }
+        }
+      };
+      load_tables(0);
+      // The query rows: 32 rows x QCH chunks over 64 lanes, every load in
+      // flight at once.
+      constexpr int NQL = QCH / 2;
+      {
+        u32x4_t qv[NQL];
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const int idx = (q0 + q) * 64 + ln;
+        for (int q = 0; q < NQL; ++q) {
+          const int idx = q * 64 + ln;
           const int r = idx / QCH;
           const int c0 = (idx - r * QCH) * 8;
           qv[q] = u32x4_t{0u, 0u, 0u, 0u};
-          if (q0 + q < NQL && w * 32 + r < t.nrows && c0 < p.hs)
+          if (w * 32 + r < t.nrows && c0 < p.hs)
             qv[q] = *(const u32x4_t*)(p.query + head_row(p, t, t.row0 + w * 32 + r) * p.hs + c0);
         }
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const int idx = (q0 + q) * 64 + ln;
+        for (int q = 0; q < NQL; ++q) {
+          const int idx = q * 64 + ln;
           const int r = idx / QCH;
-          if (q0 + q < NQL) *(u32x4_t*)qel(r, (idx - r * QCH) * 8) = qv[q];
+          *(u32x4_t*)qel(r, (idx - r * QCH) * 8) = qv[q];
         }
       }
       __syncthreads();
-      if (p.do_rotary) {
-        // One task rotates 8 channels of a row: non-interleaved, channels
-        // ro + 8 i .. + 8 with their partners half channels later (cos/sin
-        // entries 8 i .. + 8); interleaved, the 4 pairs of channels
-        // ro + 8 j .. + 8 (entries 4 j .. + 4). Tasks go four per lane at a
-        // time, table loads first.
-        const int half = p.rd >> 1;
-        const int per_row = p.interleaved ? p.rd / 8 : half / 8;
-        const int ntask = 32 * per_row;
-        for (int tb = 0; tb < ntask; tb += 4 * 64) {
-          u32x4_t cv[4], sv[4];
-          int rr[4], gg[4];
-          bool ok[4];
+      for (int tb = 0; tb < ntask; tb += 4 * 64) {
+        if (tb > 0) load_tables(tb);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int task = tb + k * 64 + ln;
-            rr[k] = task / per_row;
-            gg[k] = task - rr[k] * per_row;
-            ok[k] = task < ntask && w * 32 + rr[k] < t.nrows;
-            cv[k] = sv[k] = u32x4_t{0u, 0u, 0u, 0u};
-            if (ok[k]) {
-              const int posr = past_b + (t.row0 + w * 32 + rr[k]) / p.H;
-              const int64_t e0 = min(max((int64_t)posr, (int64_t)0), p.prow - 1) * half;
-              if (p.interleaved) {
-                const u32x2_t c2 = *(const u32x2_t*)(p.cos_t + e0 + 4 * gg[k]);
-                const u32x2_t s2 = *(const u32x2_t*)(p.sin_t + e0 + 4 * gg[k]);
-                cv[k] = u32x4_t{c2[0], c2[1], 0u, 0u};
-                sv[k] = u32x4_t{s2[0], s2[1], 0u, 0u};
-              } else {
-                cv[k] = *(const u32x4_t*)(p.cos_t + e0 + 8 * gg[k]);
-                sv[k] = *(const u32x4_t*)(p.sin_t + e0 + 8 * gg[k]);
-              }
+        for (int k = 0; k < 4; ++k) {
+          if (!ok[k]) continue;
+          float c[8], sn[8];
+          unpack8<DT>(cv[k], c);
+          unpack8<DT>(sv[k], sn);
+          if (p.interleaved) {
+            uint16_t* e = qel(rr[k], p.ro + 8 * gg[k]);
+            float x[8];
+            unpack8<DT>(*(const u32x4_t*)e, x);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const float xe = x[2 * m], xo = x[2 * m + 1];
+              x[2 * m] = xe * c[m] - xo * sn[m];
+              x[2 * m + 1] = xo * c[m] + xe * sn[m];
             }
-          }
+            *(u32x4_t*)e = pack8<DT>(x);
+          } else {
+            uint16_t* e1 = qel(rr[k], p.ro + 8 * gg[k]);
+            uint16_t* e2 = qel(rr[k], p.ro + 8 * gg[k] + half);
+            float x1[8], x2[8], y1[8], y2[8];
+            unpack8<DT>(*(const u32x4_t*)e1, x1);
+            unpack8<DT>(*(const u32x4_t*)e2, x2);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (!ok[k]) continue;
-            float c[8], sn[8];
-            unpack8<DT>(cv[k], c);
-            unpack8<DT>(sv[k], sn);
-            if (p.interleaved) {
-              uint16_t* e = qel(rr[k], p.ro + 8 * gg[k]);
-              float x[8];
-              unpack8<DT>(*(const u32x4_t*)e, x);
-#pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                const float xe = x[2 * m], xo = x[2 * m + 1];
-                x[2 * m] = xe * c[m] - xo * sn[m];
-                x[2 * m + 1] = xo * c[m] + xe * sn[m];
-              }
-              *(u32x4_t*)e = pack8<DT>(x);
-            } else {
-              uint16_t* e1 = qel(rr[k], p.ro + 8 * gg[k]);
-              uint16_t* e2 = qel(rr[k], p.ro + 8 * gg[k] + half);
-              float x1[8], x2[8], y1[8], y2[8];
-              unpack8<DT>(*(const u32x4_t*)e1, x1);
-              unpack8<DT>(*(const u32x4_t*)e2, x2);
-#pragma unroll
-              for (int m = 0; m < 8; ++m) {
-                y1[m] = x1[m] * c[m] - x2[m] * sn[m];
-                y2[m] = x2[m] * c[m] + x1[m] * sn[m];
-              }
-              *(u32x4_t*)e1 = pack8<DT>(y1);
-              *(u32x4_t*)e2 = pack8<DT>(y2);
+            for (int m = 0; m < 8; ++m) {
+              y1[m] = x1[m] * c[m] - x2[m] * sn[m];
+              y2[m] = x2[m] * c[m] + x1[m] * sn[m];
             }
+            *(u32x4_t*)e1 = pack8<DT>(y1);
+            *(u32x4_t*)e2 = pack8<DT>(y2);
           }
         }
       }
