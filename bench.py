@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="print the markdown summary of rocprofv3 --pmc output directories (SQ/GRBM counters)")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="after the timed runs, replay the step graph for this many seconds while sampling the "
+                         "socket power with amd-smi (reported under roofline.power; 0: skip)")
     return ap.parse_args()
 
 
@@ -364,6 +367,91 @@ def flushed_steps(torch, pa, dev, steps, mib):
     return {"flush_mib": mib, "steps": steps, "phase_ms": stats(phase), "kernel_ms": stats(kern)}
 
 
+def _json_find(obj, pred):
+    """Values of the keys of a parsed JSON tree for which pred(key) holds."""
+    out = []
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            if pred(str(k).lower()):
+                out.append(v)
+            out.extend(_json_find(v, pred))
+    elif isinstance(obj, list):
+        for v in obj:
+            out.extend(_json_find(v, pred))
+    return out
+
+
+def _watts(v):
+    """A power reading as amd-smi / rocm-smi print it (a number, a string, or
+    {"value": ..., "unit": "W"}), in watts, or None."""
+    if isinstance(v, dict):
+        v = v.get("value")
+    try:
+        return float(str(v).split()[0])
+    except (TypeError, ValueError, IndexError):
+        return None
+
+
+def _smi_json(args):
+    import subprocess
+    try:
+        r = subprocess.run(args, capture_output=True, text=True, timeout=20)
+        starts = [i for i in (r.stdout.find("["), r.stdout.find("{")) if i >= 0]
+        return json.loads(r.stdout[min(starts):]) if starts else None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+
+
+def power_sample(torch, dev, steps: int, seconds: float):
+    """Sustained load: a HIP graph of `steps` steps replayed back to back for
+    `seconds` while a thread reads the socket power with amd-smi about twice a
+    second. Reports the readings, the board's power cap and the sustained
+    step time (the clock settles where the power meets the cap). The first
+    second's readings are skipped."""
+    import threading
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            dev.write()
+            dev.attention()
+    torch.cuda.synchronize()
+    readings, stop = [], threading.Event()
+
+    def sampler():
+        stop.wait(1.0)                      # readings once the load has settled
+        while not stop.is_set():
+            j = _smi_json(["amd-smi", "metric", "-p", "-g", "0", "--json"])
+            vals = [_watts(v) for v in _json_find(j, lambda k: k == "socket_power")] if j is not None else []
+            vals = [v for v in vals if v is not None]
+            if vals:
+                readings.append(vals[0])
+            stop.wait(0.5)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    g.replay()
+    torch.cuda.synchronize()
+    th.start()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    n = 0
+    a.record()
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        n += 1
+        torch.cuda.synchronize()
+    b.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    cap_j = _smi_json(["rocm-smi", "--showmaxpower", "--json"])
+    caps = [_watts(v) for v in _json_find(cap_j, lambda k: "max" in k and "power" in k)] if cap_j is not None else []
+    caps = [c for c in caps if c is not None]
+    return {"what": f"socket power (amd-smi) while a graph of {steps} steps is replayed back to back",
+            "seconds": round(seconds, 1), "samples": len(readings),
+            "socket_w": stats(readings) if readings else None, "cap_w": caps[0] if caps else None,
+            "sustained_ms_per_step": round(a.elapsed_time(b) / (n * steps), 5)}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -494,6 +582,9 @@ def main():
                    "tokens_per_s": round(w["dims"]["token_count"] / (ms_step * 1e-3), 1)},
         "roofline": roof,
     }
+    if args.power_seconds > 0:
+        roof["power"] = power_sample(torch, dev, args.steps, args.power_seconds)
+        print(f"[bench] power: {json.dumps(roof['power'])}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
