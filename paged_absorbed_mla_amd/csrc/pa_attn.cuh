@@ -86,6 +86,7 @@ struct AttnParams {
   const uint16_t* vcache;   // separate layout: value cache [slots][kvh][vhs] (null in the latent layout)
   int nblk;                 // num_blocks (< 2^31 / block_size): block ids are clamped into [0, nblk)
   int kv_stream;            // 1: every KV row is read by one query tile only (a decode-shaped call)
+  int many_pieces;          // 1: split-KV leaves many pieces per query tile (see CombineShape)
   int64_t prow;             // rotary table rows: positions are clamped into [0, prow)
   int H;                    // query heads per key/value head (rows per token of a query tile)
   int Hq;                   // query heads of the call (H * kvh): head stride of query and output rows
@@ -935,18 +936,21 @@ __device__ __forceinline__ int64_t piece_slot(const MTile& t, int q) {
 // pairs. Up to QA pieces: the pairs and all slice loads go out together (one
 // round trip). More pieces: the pairs are read QM pieces at a time, then the
 // slices QA pieces at a time with all their 16-byte loads in flight together.
-template <int VHSP>
+// MANY: the launch expects many pieces per tile (short decode batches), so
+// rows of one 8-channel group take 16 pieces per round trip (the registers
+// this holds would lower the occupancy of launches with few pieces).
+template <int VHSP, bool MANY = false>
 struct CombineShape {
   static constexpr int TPR = (VHSP / 8) < 32 ? (VHSP / 8) : 32;   // threads per row
   static constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 8)
   static constexpr int ROWS = 256 / TPR;                          // rows per block
   static constexpr int NV = CPT / 8;
-  static constexpr int QA = NV <= 2 ? 8 : 4;                      // pieces per round trip
+  static constexpr int QA = (MANY && NV == 1) ? 16 : (NV <= 2 ? 8 : 4);   // pieces per round trip
 };
 
-template <typename DT, int VHSP, int RW>
+template <typename DT, int VHSP, int RW, bool MANY = false>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  using CS = CombineShape<VHSP>;
+  using CS = CombineShape<VHSP, MANY>;
   constexpr int TPR = CS::TPR;
   constexpr int CPT = CS::CPT;
   constexpr int ROWS = CS::ROWS;
@@ -1094,8 +1098,11 @@ typedef hipError_t (*AttnOccFn)(int*);
     e = hipGetLastError();                                                                                \
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                              \
     if (e != hipSuccess || !combine) return e;                                                            \
-    combine_kernel<DT, VHSP, NW * 32>                                                                     \
-        <<<dim3(cgrid, (NW * 32 + CombineShape<VHSP>::ROWS - 1) / CombineShape<VHSP>::ROWS), 256, 0, s>>>(p);     \
+    {                                                                                                     \
+      const dim3 cg(cgrid, (NW * 32 + CombineShape<VHSP>::ROWS - 1) / CombineShape<VHSP>::ROWS);          \
+      if (CombineShape<VHSP>::NV == 1 && p.many_pieces) combine_kernel<DT, VHSP, NW * 32, true><<<cg, 256, 0, s>>>(p); \
+      else combine_kernel<DT, VHSP, NW * 32><<<cg, 256, 0, s>>>(p);                                       \
+    }                                                                                                     \
     return hipGetLastError();                                                                             \
   }                                                                                                       \
   }

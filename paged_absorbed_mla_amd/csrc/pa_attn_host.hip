@@ -631,6 +631,9 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   // query tile): each KV row is read by one query tile only, so the four-wave
   // 576/512 kernel's copies take the streaming cache policy.
   ap.kv_stream = (g.T <= g.B && ap.H <= cfg.rows()) ? 1 : 0;
+  // More than eight pieces per query tile on average (one query tile per
+  // scheduled sequence in such a call).
+  ap.many_pieces = (split_kv && ap.kv_stream && ws.grid > 8 * (int64_t)g.B * g.kvh) ? 1 : 0;
   ap.prow = g.do_rotary ? g.P : 1;
   ap.vcache = (const uint16_t*)value_cache;
   ap.Hq = g.H;
