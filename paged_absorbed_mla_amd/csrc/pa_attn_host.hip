@@ -98,7 +98,7 @@ __device__ int32_t block_exclusive_scan(int64_t n, Get get, Put put) {
 // A row whose token the sequence bounds do not place inside [0, T) (only a
 // violated precondition does that) is not stored.
 constexpr int kPreRows = 32;
-constexpr int kSchedLdsBytes = 65536;
+constexpr int kSchedLdsBytes = 40832;   // transpose buffer and staging; with the scan sums, four blocks per CU
 constexpr int kPreMaxCpr = 72;                                       // chunks per row of a 576-wide copy
 constexpr int kPreItems = (kPreRows * kPreMaxCpr + kSchedThreads - 1) / kSchedThreads;   // chunks per thread
 constexpr int kPreTBytes = kPreRows * (kPreMaxCpr | 1) * 16;         // transpose buffer
@@ -601,8 +601,9 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.interleaved = g.interleaved;
   sp.dtype = g.dtype;
   // Query pre-pass blocks: one per kPreRows query rows, at most kPrepassBlocks
-  // (two per compute unit of a 256-CU part; grid-stride loop).
-  constexpr int64_t kPrepassBlocks = 512;
+  // (four per compute unit of a 256-CU part, as many as the launch's LDS lets
+  // a CU hold; grid-stride loop).
+  constexpr int64_t kPrepassBlocks = 1024;
   const int64_t rope_groups = sp.qfrag ? (g.T * g.H + kPreRows - 1) / kPreRows : 0;
   const int64_t rope_blocks = std::min<int64_t>(rope_groups, kPrepassBlocks);
   schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
