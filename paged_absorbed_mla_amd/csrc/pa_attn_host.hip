@@ -333,6 +333,10 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
                             : (v * G + Uv - 1) / Uv;
     return (int)min(c, (int64_t)G + 1);
   };
+  // The unit range of every workgroup: each tile's thread loops over the
+  // workgroups whose cuts land in it, or, when tiles hold many ranges each
+  // (short decode batches), each range is found by its own thread.
+  const bool per_range = p.split_kv && (int64_t)G > 4 * (int64_t)M;
   for (int i = threadIdx.x; i < M; i += kSchedThreads) {
     const int b = tb[i];
     MTile t;
@@ -352,10 +356,12 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
       t.w_first = Wi + Pi - 1;
       t.npieces = Wn - t.w_first;
       t.part_base = Pi > 0 ? t.w_first : p.grid + i;   // slot of the first piece
-      for (int w = Wi; w < Wn; ++w) {
-        const int64_t o = cut(w) - Vi - alpha;
-        p.wg_range[w] = u0[i] + (int32_t)min(max(o, (int64_t)0), (int64_t)(u0[i + 1] - u0[i]));
-        p.wg_tile[w] = i;
+      if (!per_range) {
+        for (int w = Wi; w < Wn; ++w) {
+          const int64_t o = cut(w) - Vi - alpha;
+          p.wg_range[w] = u0[i] + (int32_t)min(max(o, (int64_t)0), (int64_t)(u0[i + 1] - u0[i]));
+          p.wg_tile[w] = i;
+        }
       }
     } else {
       t.w_first = i;
@@ -368,6 +374,23 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
   }
   // Workgroups past the last cut inside a tile: empty ranges at the end.
   const int wtail = p.split_kv ? (M > 0 ? cnt(Uv) : 0) : M;
+  if (per_range) {
+    // Every other range, one workgroup per thread: its cut x(w) falls in the
+    // virtual span [V_i, V_i+1) of tile i (V_i = u0[i] + alpha i, found by
+    // binary search) and starts at that tile's unit x(w) - V_i - alpha,
+    // clamped into the tile's units.
+    for (int w = threadIdx.x; w < wtail; w += kSchedThreads) {
+      const int64_t x = cut(w);
+      int lo = 0, hi = M - 1;                          // last i with V_i <= x (V_0 = 0)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)u0[mid] + alpha * mid <= x) lo = mid; else hi = mid - 1;
+      }
+      const int64_t o = x - ((int64_t)u0[lo] + alpha * lo) - alpha;
+      p.wg_range[w] = u0[lo] + (int32_t)min(max(o, (int64_t)0), (int64_t)(u0[lo + 1] - u0[lo]));
+      p.wg_tile[w] = lo;
+    }
+  }
   for (int w = wtail + (int)threadIdx.x; w <= p.grid; w += kSchedThreads) {
     p.wg_range[w] = (int32_t)U;
     if (w < p.grid) p.wg_tile[w] = max(M - 1, 0);
