@@ -706,7 +706,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       // with the query rows (they depend only on the rows' positions), so
       // the staging waits for memory once.
       const int half = p.rd >> 1;
-      const int per_row = p.interleaved ? p.rd / 8 : half / 8;
+      // (at least 1: without rotary channels no task exists, and rr below divides by it)
+      const int per_row = max(p.interleaved ? p.rd / 8 : half / 8, 1);
       const int ntask = p.do_rotary ? 32 * per_row : 0;
       u32x4_t cv[4], sv[4];
       int rr[4], gg[4];
