@@ -31,8 +31,11 @@ HIPCC_FLAGS = [
 
 # Extra flags by source-file prefix. The four-wave 576/512 kernel keeps its PV
 # accumulators in AGPRs through inline assembly; its compiler-built MFMAs use
-# the VGPR form so S, P and the query stay in VGPRs.
-FILE_FLAGS = {"attnm_": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# the VGPR form so S, P and the query stay in VGPRs. The generic kernels use
+# the VGPR form throughout: otherwise the one-wave instances park the scores
+# and accumulators in AGPRs and copy them back for every softmax step.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"attnm_": _VGPR_FORM, "attn_": _VGPR_FORM, "attns_": _VGPR_FORM}
 
 
 def hipcc() -> str:

@@ -338,8 +338,11 @@ struct WaveState {
 // at L (CPR chunks each), V rows at LV (VCPR chunks each; LV = L when V is
 // the leading part of the latent row).
 // after_qk() runs once the QK MFMAs are queued (the caller issues the second
-// half of a later tile's copies there).
-template <typename DT, int HSP, int VHSP, int KT, int QREG, int VCPR, typename AfterQK>
+// half of a later tile's copies there). GEN: the general score map (softcap,
+// or a scale that is not positive); otherwise the raw scores go straight into
+// the exponent (the common case, compiled without the other branches so that
+// the scores stay in their registers).
+template <typename DT, int HSP, int VHSP, int KT, int QREG, int VCPR, bool GEN, typename AfterQK>
 __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>& st, const uint8_t* L,
                                              const uint8_t* LV, const uint16_t* qrest, int key0, int pos,
                                              int lo_row, bool softcap_on, bool full, const AttnParams& p,
@@ -402,40 +405,40 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   // and no softcap the raw scores stay as they are: their max, times the
   // scale, is the max of the scaled scores (rounding is monotone), and the
   // scale is applied inside the exponent (one fma per score).
-  const bool raw = !softcap_on && p.scale_log2 > 0.0f;
-  if (softcap_on) {
+  if constexpr (GEN) {
+    if (softcap_on) {
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
+      for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[sub][e] = softcap_log2(s[sub][e], p.scale, p.softcap, p.softcap_inv);
-  } else if (!raw) {
-    const float sc = p.scale_log2;
+        for (int e = 0; e < 16; ++e) s[sub][e] = softcap_log2(s[sub][e], p.scale, p.softcap, p.softcap_inv);
+    } else {
+      const float sc = p.scale_log2;
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
+      for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[sub][e] *= sc;   // element by element: a vector product would splat sc
-  }
-  const float mul = raw ? p.scale_log2 : 1.0f;
-  // `full` (wave-uniform): every row of the wave sees every key of the tile,
-  // so no key is masked.
-  float tmax = -INFINITY;
-  if (full) {
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[sub][e]);
-  } else {
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = key0 + sub * 32 + hi * 4 + (e & 3) + 8 * (e >> 2);
-        const float v = (j <= pos && j >= lo_row) ? s[sub][e] : -INFINITY;
-        s[sub][e] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int e = 0; e < 16; ++e) s[sub][e] *= sc;   // element by element: a vector product would splat sc
     }
   }
+  const float mul = GEN ? 1.0f : p.scale_log2;
+  // `full` (wave-uniform): every row of the wave sees every key of the tile,
+  // so no key is masked.
+  if (!full) {
+    // Key j = key0 + c of this lane's element is visible iff lo_row <= j <= pos,
+    // i.e. c in [lo_row - key0, pos - key0] (c a compile-time constant).
+    const int chi = pos - key0 - hi * 4, clo = lo_row - key0 - hi * 4;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = sub * 32 + (e & 3) + 8 * (e >> 2);
+        s[sub][e] = (c <= chi && c >= clo) ? s[sub][e] : -INFINITY;
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[sub][e]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * mul;   // -inf stays -inf (mul > 0)
   // Lazy rescale: the reference max moves only when the tile max exceeds it by
   // more than 8 (log2 units), so probabilities stay <= 2^8, and the O
@@ -447,6 +450,8 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   const float corr = fast_exp2(st.m_run - m_use);
   const bool rescale = bump && (st.m_run != -INFINITY);
   st.m_run = m_new;
+  // The row sum adds the rounded probabilities (two per dot2 against (1, 1)),
+  // the same values the PV product weights the rows with.
   u32x4_t pf[NSUB][2];
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four partial sums: short dependency chains
 #pragma unroll
@@ -455,11 +460,10 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     for (int k2 = 0; k2 < 2; ++k2) {
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = fast_exp2(__builtin_fmaf(s[sub][8 * k2 + e], mul, -m_use));
-        ps[e & 3] += pv[e];
-      }
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[sub][8 * k2 + e], mul, -m_use));
       pf[sub][k2] = pack8<DT>(pv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ps[k] = DT::sum2(pf[sub][k2][k], ps[k]);
     }
   }
   const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
@@ -516,7 +520,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
 // SEP: separate (grouped-query) layout -- K rows from the key cache, V rows
 // from the value cache into a second part of each LDS buffer; otherwise V is
 // the leading VHSP channels of the latent row already in the buffer.
-template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG, bool SEP>
+template <typename DT, int HSP, int VHSP, int NW, int KT, int QREG, bool SEP, bool GEN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1))) void attn_kernel(AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = HSP / 8;          // 16-byte chunks per LDS row
@@ -843,7 +847,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
         // then copies them at every iteration.
         const uint8_t* buf = lds_raw + bufi * BUF_BYTES;
         const bool full = wave_active && tt * KT >= lo_max_w && tt * KT + KT - 1 <= pos_min_w;
-        tile_compute<DT, HSP, VHSP, KT, QREG, VCPR>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
+        tile_compute<DT, HSP, VHSP, KT, QREG, VCPR, GEN>(st, buf, buf + (SEP ? TILE_CHUNKS * 16 : 0), qrest, tt * KT,
                                                     pos, lo_row, softcap_on, full, p, [&]() {
                                                       if (next) issue_groups(tt + NBUF - 1, nbuf, IGH{}, IGW{});
                                                     });
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
               *(f32x4_t*)((float*)p.part_o + off) = f32x4_t{x0, x1, x2, x3};
             } else {
               *(u32x2_t*)((uint16_t*)p.part_o + off) =
-                  u32x2_t{DT::from_f32(x0) | (DT::from_f32(x1) << 16), DT::from_f32(x2) | (DT::from_f32(x3) << 16)};
+                  u32x2_t{DT::pack2(x0, x1), DT::pack2(x2, x3)};
             }
           }
         }
@@ -1088,14 +1092,17 @@ typedef hipError_t (*AttnOccFn)(int*);
 #define PA_DEFINE_ATTN_INSTANCE(LAY, DT, DTN, HSP, VHSP, NW, KT, QREG)                                      \
   namespace pa {                                                                                          \
   hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, occ)(int* n) {                                       \
-    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY>;                      \
+    void (*fn)(AttnParams) = attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY, false>;               \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, reinterpret_cast<const void*>(fn), NW * 64, 0);   \
   }                                                                                                       \
   hipError_t PA_ATTN_FN(LAY, DTN, HSP, VHSP, NW, KT, launch)(const AttnParams& p, int grid, bool combine,  \
                                                              int cgrid, hipStream_t s, const hipEvent_t* ev) { \
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;                                            \
     if (e != hipSuccess) return e;                                                                        \
-    attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY><<<grid, NW * 64, 0, s>>>(p);                   \
+    if (p.softcap > 0.0f || !(p.scale_log2 > 0.0f))                                                       \
+      attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY, true><<<grid, NW * 64, 0, s>>>(p);           \
+    else                                                                                                  \
+      attn_kernel<DT, HSP, VHSP, NW, KT, QREG, PA_SEP_##LAY, false><<<grid, NW * 64, 0, s>>>(p);          \
     e = hipGetLastError();                                                                                \
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);                                              \
     if (e != hipSuccess || !combine) return e;                                                            \

@@ -335,8 +335,8 @@ __device__ __forceinline__ void mla_sm_chunk(MlaState<HSP, VHSP>& st, MlaSm& sm,
     const float mul = fused ? p.scale_log2 : 1.0f;
     const float p0 = fast_exp2(__builtin_fmaf(sm.s[2 * k], mul, -sm.m_use));
     const float p1 = fast_exp2(__builtin_fmaf(sm.s[2 * k + 1], mul, -sm.m_use));
-    sm.psum += p0 + p1;
-    sm.pf[k >> 2][k & 3] = DT::from_f32(p0) | (DT::from_f32(p1) << 16);
+    sm.pf[k >> 2][k & 3] = DT::pack2(p0, p1);
+    sm.psum = DT::sum2(sm.pf[k >> 2][k & 3], sm.psum);   // the rounded pair, as the PV product sees it
   } else if constexpr (C == 11) {
     st.l_run += sm.psum;
   }

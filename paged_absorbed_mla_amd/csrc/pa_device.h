@@ -13,6 +13,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Storage-type tags. Raw 16-bit patterns travel as uint16_t; conversions round
 // to nearest even (the page's kernel stores with __float2half_rn /
@@ -21,6 +24,14 @@ struct BF16 {
   static __device__ __forceinline__ float to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
   static __device__ __forceinline__ uint32_t from_f32(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  // (a, b) rounded and packed, a in the low half: one v_cvt_pk_bf16_f32.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  }
+  // acc + lo + hi of a packed pair (one v_dot2 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
   }
   static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -38,6 +49,12 @@ struct F16 {
   }
   static __device__ __forceinline__ uint32_t from_f32(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
   }
   static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
@@ -62,7 +79,7 @@ template <typename DT>
 __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
   u32x4_t v;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = DT::from_f32(x[2 * k]) | (DT::from_f32(x[2 * k + 1]) << 16);
+  for (int k = 0; k < 4; ++k) v[k] = DT::pack2(x[2 * k], x[2 * k + 1]);
   return v;
 }
 
