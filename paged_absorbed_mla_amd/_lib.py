@@ -72,7 +72,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    # PA_LATENT_LIB: path of another build of the same library (A/B timing of
+    # compile-time variants); the in-tree build otherwise.
+    path = path or os.environ.get("PA_LATENT_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_absorbed_mla_amd.build`")
     lib = ctypes.CDLL(path)

@@ -98,6 +98,30 @@ struct AttnParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Build-time tunables of the generic kernel (defaults measured best; other
+// values for A/B timing): fragment prefetch depths of the tile computation
+// (K fragments for QK, V^T fragments for PV) and LDS tile buffers (one-wave
+// instances, four-wave instances) where two workgroups still fit in a CU.
+#ifndef PA_GEN_QPF
+#define PA_GEN_QPF 4
+#endif
+#ifndef PA_GEN_VPF
+#define PA_GEN_VPF 3
+#endif
+#ifndef PA_GEN_NBUF
+#define PA_GEN_NBUF 3
+#endif
+#ifndef PA_GEN_NBUF4
+#define PA_GEN_NBUF4 3
+#endif
+// Wave priority: 1 raises it for the MFMA phases of a tile (QK, PV) and drops
+// it for the softmax, so that of the two workgroups sharing a CU the one with
+// matrix work issues first and the other's vector work fills the gaps between
+// its MFMAs; 0 alternates it every tile instead (four-wave instances).
+#ifndef PA_GEN_PRIO
+#define PA_GEN_PRIO 1
+#endif
+
 // Element type of the split-KV partial outputs. bfloat16 outputs keep them in
 // bfloat16: a second rounding (half an ulp, 2^-8 relative at most) stays well
 // inside that type's output tolerance. float16 outputs keep them in float32:
@@ -368,7 +392,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
   // wave's persistent LDS rows (row l32, stride QRS elements).
   constexpr int NKR = QREG / 16;
   constexpr int QRS = HSP - QREG + 8;
-  constexpr int QPF = 4;
+  constexpr int QPF = PA_GEN_QPF;
   constexpr int QSTEPS = NSUB * NKK;
   f32x16_t s[NSUB];
 #pragma unroll
@@ -382,6 +406,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     const int kk = n % NKK;
     return *(const u32x4_t*)(qrow_lds + 16 * (kk - NKR));
   };
+  if constexpr (PA_GEN_PRIO == 1) asm volatile("s_setprio 1");
   u32x4_t qa[QPF], qq[QPF];
 #pragma unroll
   for (int n = 0; n < QPF; ++n) {
@@ -399,6 +424,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     s[n / NKK] = DT::mfma32(cur, bq, s[n / NKK]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (PA_GEN_PRIO == 1) asm volatile("s_setprio 0");
   after_qk();
   // Scores into log2 units, mask, tile max. Lane holds keys
   // hi*4 + (e&3) + 8*(e>>2) (+32 sub) of its row l32. With a positive scale
@@ -492,7 +518,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     vb[0][par] = LV + k0b * VCPR * 16 + (((4 * par + lcb) ^ sw0) << 4) + (cq & 1) * 8;
     vb[1][par] = LV + (k0b + 8) * VCPR * 16 + (((4 * par + lcb) ^ sw1) << 4) + (cq & 1) * 8;
   }
-  constexpr int VPF = 3;
+  constexpr int VPF = PA_GEN_VPF;
   constexpr int VSTEPS = NSUB * 2 * NMT;
   auto pv_frag = [&](int n) -> u32x4_t {
     const int step = n / NMT, mt = n % NMT;        // step = sub * 2 + k2
@@ -503,6 +529,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     const u32x2_t d1 = __builtin_bit_cast(u32x2_t, r1);
     return u32x4_t{d0[0], d0[1], d1[0], d1[1]};
   };
+  if constexpr (PA_GEN_PRIO == 1) asm volatile("s_setprio 1");
   u32x4_t va[VPF];
 #pragma unroll
   for (int n = 0; n < VPF; ++n) va[n] = pv_frag(n);
@@ -514,6 +541,7 @@ __device__ __forceinline__ void tile_compute(WaveState<DT, HSP, VHSP, KT, QREG>&
     st.o[n % NMT] = DT::mfma32(cur, pf[step >> 1][step & 1], st.o[n % NMT]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (PA_GEN_PRIO == 1) asm volatile("s_setprio 0");
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -545,7 +573,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   constexpr int BUF_BYTES = (TILE_CHUNKS + VTILE_CHUNKS) * 16;   // K rows, then (SEP) V rows
   // Tile buffers: NBUF - 1 tiles are in flight while one is computed. Three
   // when two workgroups still fit in a CU's 160 KB of LDS, else two.
-  constexpr int NBUF = (2 * 3 * BUF_BYTES <= 150 * 1024) ? 3 : 2;
+  constexpr int NBUF_WANT = NW >= 4 ? PA_GEN_NBUF4 : PA_GEN_NBUF;
+  constexpr int NBUF = (2 * NBUF_WANT * BUF_BYTES <= 150 * 1024) ? NBUF_WANT : 2;
   constexpr int PER = LOADS + VLOADS;   // copy instructions per wave and tile (vmcnt counts them)
   constexpr int QSTAGE_BYTES = RW * QSTRIDE * 2;
   // When the staged query fits in one tile buffer it is staged in the last
@@ -823,7 +852,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       // This wave's copies of tile tt are done once at most (tiles issued
       // after it) * PER copies remain in flight; the barrier then makes every
       // wave's copies of tile tt visible.
-      if constexpr (NW >= 4) {
+      if constexpr (NW >= 4 && PA_GEN_PRIO == 0) {
         // Two workgroups share a CU (one wave of each per SIMD). With equal
         // priorities the SIMDs favour the older wave, so the workgroups of
         // the grid's first half ran ahead and those of the second half

@@ -493,7 +493,17 @@ static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
 // four-wave (prefill) instances, where a workgroup often holds several short
 // pieces; the one-wave decode pieces are long and their staging overlaps the
 // first tile copies.
-static int generic_piece_units(int nw) { return nw >= 4 ? 4 : 2; }
+// (Build-time tunables for A/B timing; the defaults are the measured best.)
+#ifndef PA_GEN_PIECE4
+#define PA_GEN_PIECE4 4
+#endif
+#ifndef PA_MLA_PIECE
+#define PA_MLA_PIECE 10
+#endif
+#ifndef PA_GEN_PIECE1
+#define PA_GEN_PIECE1 2
+#endif
+static int generic_piece_units(int nw) { return nw >= 4 ? PA_GEN_PIECE4 : PA_GEN_PIECE1; }
 
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   // Head-size buckets of the compiled instances; smaller sizes run zero-padded.
@@ -513,7 +523,7 @@ bool choose_config(const CallGeom& g, AttnConfig* cfg) {
   }
   if (g.hs <= 64 && g.vhs <= 32) { cfg->hsp = 64; cfg->vhsp = 32; cfg->kt = 32; }
   else if (g.hs <= 192 && g.vhs <= 128) { cfg->hsp = 192; cfg->vhsp = 128; cfg->kt = 64; }
-  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = 10; }
+  else if (g.hs <= 576 && g.vhs <= 512) { cfg->hsp = 576; cfg->vhsp = 512; cfg->kt = 32; cfg->wide = 2; cfg->nw = 4; cfg->piece_units = PA_MLA_PIECE; }
   else return false;
   // Four waves (128 rows) when sequences bring many query rows, one wave otherwise.
   if (!cfg->wide) {
