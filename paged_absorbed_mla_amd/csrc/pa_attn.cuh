@@ -121,6 +121,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 #ifndef PA_GEN_PRIO
 #define PA_GEN_PRIO 1
 #endif
+// Split-KV combine shape: threads per row (at most), pieces per memory round trip.
+#ifndef PA_COMB_TPR
+#define PA_COMB_TPR 64
+#endif
+#ifndef PA_COMB_QA
+#define PA_COMB_QA 4
+#endif
 
 // Element type of the split-KV partial outputs. bfloat16 outputs keep them in
 // bfloat16: a second rounding (half an ulp, 2^-8 relative at most) stays well
@@ -975,11 +982,11 @@ __device__ __forceinline__ int64_t piece_slot(const MTile& t, int q) {
 // this holds would lower the occupancy of launches with few pieces).
 template <int VHSP, bool MANY = false>
 struct CombineShape {
-  static constexpr int TPR = (VHSP / 8) < 32 ? (VHSP / 8) : 32;   // threads per row
+  static constexpr int TPR = (VHSP / 8) < PA_COMB_TPR ? (VHSP / 8) : PA_COMB_TPR;   // threads per row
   static constexpr int CPT = VHSP / TPR;                          // channels per thread (multiple of 8)
   static constexpr int ROWS = 256 / TPR;                          // rows per block
   static constexpr int NV = CPT / 8;
-  static constexpr int QA = (MANY && NV == 1) ? 16 : (NV <= 2 ? 8 : 4);   // pieces per round trip
+  static constexpr int QA = (MANY && NV == 1) ? 16 : (NV <= 2 ? PA_COMB_QA : 4);   // pieces per round trip
 };
 
 template <typename DT, int VHSP, int RW, bool MANY = false>
