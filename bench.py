@@ -3,7 +3,9 @@
 
 A step is one pass of the whole path over one batch: the write phase (RoPE +
 scatter of the new latent rows) followed by the attention phase (on-device
-schedule, MFMA attention, split-KV combine). The default workload is the
+schedule, MFMA attention, split-KV combine); in the latent layout both run in
+one fused call (pa_latent_forward), whose first launch carries the write rows
+beside the schedule. The default workload is the
 DeepSeek-V3-dims absorbed MLA decode batch: bf16, 64 sequences with one new
 token each, past lengths uniform in [4096, 16384], 128 heads, latent 576,
 value 512, rotary 64 at offset 512, block size 64, random block permutation,
@@ -61,6 +63,9 @@ def parse():
     ap.add_argument("--flush-steps", type=int, default=20,
                     help="extra steps, each after a MALL flush, for per-step statistics (0: none)")
     ap.add_argument("--flush-mib", type=int, default=512, help="scratch written before each flushed step")
+    ap.add_argument("--calls", default="fused", choices=["fused", "separate"],
+                    help="latent layout: a step as one fused call (pa_latent_forward) or as pa_latent_write "
+                         "followed by pa_latent_attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -293,6 +298,25 @@ def stats(xs):
             "p10": round(float(np.percentile(a, 10)), 5), "p90": round(float(np.percentile(a, 90)), 5)}
 
 
+def step_with_events(pa, dev, s, a, b, ka, kb):
+    """One step with events a/b around its attention phase and ka/kb (recorded
+    by the library on its launch stream) around the attention kernel. In the
+    latent layout the step is the fused call (pa_latent_forward: the write rows
+    run in the attention phase's first launch), so a/b bracket the whole call;
+    in the separate layout the write is its own call before a."""
+    if not dev.fused:
+        dev.write()
+        a.record(s)
+        pa.pa_latent_profile_next(ka, kb)
+        dev.attention()
+        b.record(s)
+    else:
+        a.record(s)
+        pa.pa_latent_profile_next(ka, kb)
+        dev.forward()
+        b.record(s)
+
+
 def timed_steps(torch, pa, dev, steps, graph):
     """K back-to-back steps (write + attention) bracketed by events, with events
     around each attention phase and, recorded by the library on its launch
@@ -311,11 +335,7 @@ def timed_steps(torch, pa, dev, steps, graph):
         # (inside a graph capture the events become graph nodes; only the
         # bracketing events outside the graph are read then)
         for k in range(steps):
-            dev.write()
-            ev[k][0].record(s)
-            pa.pa_latent_profile_next(kev[k][0], kev[k][1])
-            dev.attention()
-            ev[k][1].record(s)
+            step_with_events(pa, dev, s, ev[k][0], ev[k][1], kev[k][0], kev[k][1])
 
     start_all = torch.cuda.Event(enable_timing=True)
     end_all = torch.cuda.Event(enable_timing=True)
@@ -355,11 +375,7 @@ def flushed_steps(torch, pa, dev, steps, mib):
         ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ka.record(stream)
         kb.record(stream)
-        dev.write()
-        a.record(stream)
-        pa.pa_latent_profile_next(ka, kb)
-        dev.attention()
-        b.record(stream)
+        step_with_events(pa, dev, stream, a, b, ka, kb)
         torch.cuda.synchronize()
         phase.append(a.elapsed_time(b))
         kern.append(ka.elapsed_time(kb))
@@ -412,8 +428,7 @@ def power_sample(torch, dev, steps: int, seconds: float):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(steps):
-            dev.write()
-            dev.attention()
+            dev.step()
     torch.cuda.synchronize()
     readings, stop = [], threading.Event()
 
@@ -492,6 +507,7 @@ def main():
     print(f"[bench] workload {args.config} generated in {time.perf_counter() - t_gen:.1f} s: "
           f"T={w['dims']['token_count']} B={w['dims']['batch']} kv_rows={counts['kv_rows']}", file=sys.stderr, flush=True)
     dev = DeviceWorkload(w, "cuda:0")
+    dev.fused = dev.fused and args.calls == "fused"
     for _ in range(args.warmup):
         dev.step()
     torch.cuda.synchronize()
@@ -552,10 +568,14 @@ def main():
         "kernel_ms": stats(kern_ms),
         "alg_bytes_per_launch": int(byts), "alg_flops_per_launch": int(flops),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-        "phase": dict({"what": "attention call: schedule launch + attention kernel + combine (events around "
-                               "the call)", "avg_ms": round(attn_avg_ms, 5), "ms": stats(attn_ms)},
+        "phase": dict({"what": ("attention call: schedule launch + attention kernel + combine (events around "
+                                "the call)") if not dev.fused else
+                               ("fused call (pa_latent_forward): schedule launch carrying the write rows + "
+                                "attention kernel + combine (events around the call)"),
+                       "avg_ms": round(attn_avg_ms, 5), "ms": stats(attn_ms)},
                       **side(attn_avg_ms)),
-        "step": dict({"what": f"write + attention, whole-job time / steps ({args.launch} launch)",
+        "step": dict({"what": f"write + attention ({'one fused call' if dev.fused else 'two calls'}), whole-job "
+                              f"time / steps ({args.launch} launch)",
                       "ms": round(ms_step, 5), "eager_ms": round(ms_step_e, 5)}, **side(ms_step)),
     })
     if flushed is not None:
@@ -574,6 +594,7 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded)",
         "launch": args.launch,
+        "calls": "fused" if dev.fused else "separate",
         "config": {"workload": WORKLOADS[args.config], "tokens": w["dims"]["token_count"],
                    "batch": w["dims"]["batch"], "num_heads": w["attrs"]["num_heads"],
                    "head_size": w["attrs"]["head_size"], "v_head_size": w["attrs"]["v_head_size"],

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_LATENT_ABI_VERSION 2
+#define PA_LATENT_ABI_VERSION 3
 
 typedef enum {
   PA_OK = 0,
@@ -186,6 +186,27 @@ pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims
                               const void* sin_cache, const int32_t* cumulative_sequence_length,
                               const int32_t* past_seqlens, const int32_t* block_table, void* output,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Both phases in one call: pa_latent_write then pa_latent_attention on the
+ * same stream, as the op's execute step enqueues its write kernel and then
+ * its attention kernel for one set of inputs (docs.rs page, host function
+ * execute; "LATENT semantics": the write phase places the new rows, the read
+ * phase then attends over them). The results are those of the two calls
+ * made in that order, bit for bit; the write's rows run in the read phase's
+ * first launch (the on-device schedule, which reads none of what the write
+ * stores), which saves one launch per step. Arguments are the union of the
+ * two calls' (same meaning, layout and ownership; key_cache is updated in
+ * place and then read), with the workspace of pa_latent_attention
+ * (pa_latent_workspace_size). Every check of both calls runs before anything
+ * is enqueued. Returns PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_NOT_IMPLEMENTED,
+ * PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_CAPTURE_NOT_WARMED or PA_ERR_DEVICE.
+ */
+pa_status pa_latent_forward(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                            const void* query, const void* key, const void* cos_cache, const void* sin_cache,
+                            const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
+                            const int32_t* past_seqlens, const int32_t* block_table, void* key_cache,
+                            void* output, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_latent_attention with the split-KV partition chosen by the caller:

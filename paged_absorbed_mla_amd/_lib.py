@@ -25,7 +25,7 @@ PA_ERR_CAPTURE_NOT_WARMED = 5
 PA_F16 = 10
 PA_BF16 = 16
 
-EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention",
+EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention", "pa_latent_forward",
             "pa_latent_attention_splits", "pa_latent_attention_noalloc", "pa_latent_capture_ready",
             "pa_separate_write", "pa_separate_workspace_size", "pa_separate_attention",
             "pa_latent_profile_next", "pa_last_error", "pa_latent_abi_version")
@@ -86,6 +86,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_latent_workspace_size.restype = ctypes.c_int
     lib.pa_latent_attention.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_latent_attention.restype = ctypes.c_int
+    lib.pa_latent_forward.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pa_latent_forward.restype = ctypes.c_int
     lib.pa_latent_attention_splits.argtypes = [A, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                ctypes.c_int32, vp]
     lib.pa_latent_attention_splits.restype = ctypes.c_int
@@ -176,6 +178,18 @@ def pa_latent_attention(attrs, dims, dtype, query, key_cache, cos_cache, sin_cac
                                  _ptr(cumulative_sequence_length), _ptr(past_seqlens), _ptr(block_table),
                                  _ptr(output), _ptr(workspace), int(workspace_bytes),
                                  _stream(stream, output, query))
+    return _check(st) if check else st
+
+
+def pa_latent_forward(attrs, dims, dtype, query, key, cos_cache, sin_cache, slot_mapping,
+                      cumulative_sequence_length, past_seqlens, block_table, key_cache, output, workspace,
+                      workspace_bytes, stream=None, check=True):
+    lib = load()
+    st = lib.pa_latent_forward(ctypes.byref(attrs), ctypes.byref(dims), int(dtype), _ptr(query), _ptr(key),
+                               _ptr(cos_cache), _ptr(sin_cache), _ptr(slot_mapping),
+                               _ptr(cumulative_sequence_length), _ptr(past_seqlens), _ptr(block_table),
+                               _ptr(key_cache), _ptr(output), _ptr(workspace), int(workspace_bytes),
+                               _stream(stream, output, query))
     return _check(st) if check else st
 
 

@@ -154,7 +154,7 @@ pa_status device_error(hipError_t e, const char* what) {
 // device: the first eager call is where the library's one-time host work
 // happens (occupancy query, code-object load on the device, the static
 // scratch address), none of which may run inside a capture.
-enum Phase { kWrite = 0, kAttention = 1, kAttentionNoAlloc = 2 };
+enum Phase { kWrite = 0, kAttention = 1, kAttentionNoAlloc = 2, kForward = 3 };
 
 struct Signature {
   int32_t device, phase, dtype, split, kvh;
@@ -216,7 +216,8 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
                          const void* query, const void* key_cache, const void* cos_cache, const void* sin_cache,
                          const int32_t* cumseq, const int32_t* past, const int32_t* block_table, void* output,
                          void* workspace, size_t workspace_bytes, bool split_kv, void* stream,
-                         int phase = kAttention, int kvh = 0, const void* value_cache = nullptr) {
+                         int phase = kAttention, int kvh = 0, const void* value_cache = nullptr,
+                         const pa::FusedWrite* fw = nullptr) {
   hipEvent_t ev[2] = {g_prof_ev[0], g_prof_ev[1]};
   g_prof_ev[0] = g_prof_ev[1] = nullptr;
   const bool timed = ev[0] != nullptr && ev[1] != nullptr;
@@ -233,6 +234,10 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   if ((st = check_ptr(output, "output", any)) != PA_OK) return st;
   if ((st = check_ptr(cos_cache, "cos_cache", any && g.do_rotary)) != PA_OK) return st;
   if ((st = check_ptr(sin_cache, "sin_cache", any && g.do_rotary)) != PA_OK) return st;
+  if (fw) {
+    if ((st = check_ptr(fw->key, "key", any)) != PA_OK) return st;
+    if ((st = check_ptr(fw->slot_mapping, "slot_mapping", any)) != PA_OK) return st;
+  }
   pa::AttnConfig cfg;
   if (!pa::choose_config(g, &cfg))
     return fail(PA_ERR_NOT_IMPLEMENTED, "no attention instance for head_size %d / v_head_size %d (built: %s)", g.hs,
@@ -254,7 +259,7 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   if (workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace_bytes, ws.total);
   e = pa::launch_attention(g, cfg, ws, split_kv, query, key_cache, value_cache, cos_cache, sin_cache, cumseq, past,
-                           block_table, output, workspace, (hipStream_t)stream, timed ? ev : nullptr);
+                           block_table, output, workspace, (hipStream_t)stream, timed ? ev : nullptr, fw);
   if (e != hipSuccess) return device_error(e, "attention launch");
   if (!capturing) mark_warmed(sig);
   g_last_error.clear();
@@ -357,6 +362,17 @@ pa_status pa_latent_attention(const pa_latent_attrs* attrs, const pa_latent_dims
                               void* workspace, size_t workspace_bytes, void* stream) {
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, workspace, workspace_bytes, true, stream);
+}
+
+pa_status pa_latent_forward(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
+                            const void* query, const void* key, const void* cos_cache, const void* sin_cache,
+                            const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
+                            const int32_t* past_seqlens, const int32_t* block_table, void* key_cache, void* output,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const pa::FusedWrite fw{key, slot_mapping, key_cache};
+  return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
+                        past_seqlens, block_table, output, workspace, workspace_bytes, true, stream, kForward, 0,
+                        nullptr, &fw);
 }
 
 pa_status pa_latent_attention_splits(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,

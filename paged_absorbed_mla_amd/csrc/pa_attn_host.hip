@@ -8,6 +8,7 @@
 // comment "Capture safety": geometry fixed by tensor shapes, positions and
 // blocks resolved on device).
 #include "pa_attn.cuh"
+#include "pa_write.cuh"
 
 #include <algorithm>
 #include <mutex>
@@ -39,6 +40,15 @@ struct SchedParams {
   int32_t* wg_tile;
   int32_t* sched;    // global scratch for the arrays below when they exceed kSchedLdsInts
   MTile* mt;
+  int rope_blocks;   // blocks 1 .. rope_blocks: the query pre-pass
+  // Fused call (write phase in the same launch): blocks wblock0 .. wblock0 +
+  // wblocks - 1 write token rows 4 (block - wblock0) .. + 3, one per wave,
+  // from wkey into wcache (wslots cache rows); wblocks = 0 otherwise.
+  const uint16_t* wkey;
+  const int32_t* wslot;
+  uint16_t* wcache;
+  int64_t wslots;
+  int wblock0, wblocks;
 };
 
 constexpr int kSchedThreads = 256;
@@ -407,6 +417,22 @@ __device__ __forceinline__ void schedule_build(const SchedParams& p, int32_t* ld
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kSchedLdsBytes];
+  if (p.wblocks > 0 && (int)blockIdx.x >= p.wblock0) {
+    // Write phase of a fused call: it reads none of what the schedule and the
+    // query pre-pass produce, and the attention launch that reads the rows it
+    // stores follows this launch on the stream.
+    const int64_t t = (int64_t)(blockIdx.x - p.wblock0) * (kSchedThreads / 64) + (threadIdx.x >> 6);
+    if (t < p.T) {
+      const int hs = p.hs;
+      if (p.dtype == 16)
+        write_row<BF16>(p.wkey, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, p.wcache, t, hs, hs, p.ro, p.rd,
+                        p.rd > 0, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
+      else
+        write_row<F16>(p.wkey, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, p.wcache, t, hs, hs, p.ro, p.rd,
+                       p.rd > 0, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
+    }
+    return;
+  }
   if (blockIdx.x > 0) {
     // Sequence bounds staged behind the transpose buffer when they fit (one
     // coalesced load per block instead of chains of dependent global loads).
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     const int32_t* cum = staged ? stage : p.cumseq;
     const int32_t* pst = staged ? stage + p.B + 1 : p.past;
     const int64_t groups = (p.T * p.H + kPreRows - 1) / kPreRows;
-    for (int64_t gi = blockIdx.x - 1; gi < groups; gi += gridDim.x - 1) {
+    for (int64_t gi = blockIdx.x - 1; gi < groups; gi += p.rope_blocks) {
       if (p.dtype == 16) query_frag_rows<BF16>(p, gi * kPreRows, lds, cum, pst);
       else query_frag_rows<F16>(p, gi * kPreRows, lds, cum, pst);
     }
@@ -595,7 +621,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
                             const void* query, const void* cache, const void* value_cache, const void* cos_t,
                             const void* sin_t, const int32_t* cumseq, const int32_t* past,
                             const int32_t* block_table, void* out, void* workspace, hipStream_t stream,
-                            const hipEvent_t* ev) {
+                            const hipEvent_t* ev, const FusedWrite* fw) {
   if (g.T == 0) return hipSuccess;
   const InstanceEntry* e = find_instance(g.dtype, cfg);
   if (!e) return hipErrorInvalidValue;
@@ -639,7 +665,16 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   constexpr int64_t kPrepassBlocks = 1024;
   const int64_t rope_groups = sp.qfrag ? (g.T * g.H + kPreRows - 1) / kPreRows : 0;
   const int64_t rope_blocks = std::min<int64_t>(rope_groups, kPrepassBlocks);
-  schedule_kernel<<<(unsigned)(1 + rope_blocks), kSchedThreads, 0, stream>>>(sp);
+  sp.rope_blocks = (int)rope_blocks;
+  // Write rows of a fused call: four per block (one per wave), after the
+  // pre-pass blocks.
+  sp.wkey = fw ? (const uint16_t*)fw->key : nullptr;
+  sp.wslot = fw ? fw->slot_mapping : nullptr;
+  sp.wcache = fw ? (uint16_t*)fw->key_cache : nullptr;
+  sp.wslots = g.NB * g.bs;
+  sp.wblock0 = (int)(1 + rope_blocks);
+  sp.wblocks = fw ? (int)((g.T + kSchedThreads / 64 - 1) / (kSchedThreads / 64)) : 0;
+  schedule_kernel<<<(unsigned)(1 + rope_blocks + sp.wblocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

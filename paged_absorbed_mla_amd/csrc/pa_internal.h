@@ -61,12 +61,22 @@ hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, 
 
 WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv);
 
+// Write phase carried by the attention phase's schedule launch (the fused
+// call, latent layout): key rows [T, hs] into key_cache at slot_mapping.
+struct FusedWrite {
+  const void* key;
+  const int32_t* slot_mapping;
+  void* key_cache;
+};
+
 // Attention phase: schedule, attention, combine (three launches). `ev`: null, or
 // two events recorded right before and after the attention kernel's launch.
+// `fw`: null, or the write phase to run in the schedule launch (before the
+// attention kernel reads the cache).
 hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLayout& ws, bool split_kv,
                             const void* query, const void* cache, const void* value_cache, const void* cos_t,
                             const void* sin_t, const int32_t* cumseq, const int32_t* past,
                             const int32_t* block_table, void* out, void* workspace, hipStream_t stream,
-                            const hipEvent_t* ev);
+                            const hipEvent_t* ev, const FusedWrite* fw = nullptr);
 
 }  // namespace pa

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pa.pa_latent_abi_version() == 2
+    assert pa.pa_latent_abi_version() == 3
 
 
 def glm_attrs(**kw):
@@ -61,6 +61,15 @@ def write(a, d=None, dtype=pa.PA_BF16, ptrs=None):
     p.update(ptrs or {})
     return pa.pa_latent_write(a, d or dims(), dtype, p["key"], p["cos"], p["sin"], p["slot"], p["cumseq"],
                               p["past"], p["cache"], stream=0, check=False)
+
+
+def forward(a, d=None, dtype=pa.PA_BF16, ptrs=None, ws=DUMMY, ws_bytes=1 << 30):
+    p = dict(query=DUMMY, key=DUMMY, cos=DUMMY, sin=DUMMY, slot=DUMMY, cumseq=DUMMY, past=DUMMY, bt=DUMMY,
+             cache=DUMMY, out=DUMMY)
+    p.update(ptrs or {})
+    return pa.pa_latent_forward(a, d or dims(), dtype, p["query"], p["key"], p["cos"], p["sin"], p["slot"],
+                                p["cumseq"], p["past"], p["bt"], p["cache"], p["out"], ws, ws_bytes, stream=0,
+                                check=False)
 
 
 CASES = [
@@ -91,7 +100,7 @@ CASES = [
 def test_rejections_before_launch(desc, akw, dkw, dtype, status, frag):
     a = glm_attrs(**akw)
     d = dims(**dkw)
-    for fn in (attn, write):
+    for fn in (attn, write, forward):
         st = fn(a, d, dtype)
         assert st == status, (desc, fn.__name__, pa.pa_last_error())
         assert frag in pa.pa_last_error(), pa.pa_last_error()
@@ -107,6 +116,14 @@ def test_attention_rejects_null_required_input(which):
 @pytest.mark.parametrize("which", ["key", "slot", "cumseq", "past", "cache", "cos", "sin"])
 def test_write_rejects_null_required_input(which):
     st = write(glm_attrs(), ptrs={which: None})
+    assert st == pa.PA_ERR_INVALID_ARGUMENT
+    assert "NULL" in pa.pa_last_error()
+
+
+@pytest.mark.parametrize("which", ["query", "key", "slot", "cumseq", "past", "bt", "cache", "out", "cos", "sin"])
+def test_forward_rejects_null_required_input(which):
+    """The fused call checks the inputs of both phases before anything is enqueued."""
+    st = forward(glm_attrs(), ptrs={which: None})
     assert st == pa.PA_ERR_INVALID_ARGUMENT
     assert "NULL" in pa.pa_last_error()
 

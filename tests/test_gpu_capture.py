@@ -62,6 +62,37 @@ def test_capture_three_replays_bit_equal_to_eager(cfg, sd):
     del g
 
 
+@pytest.mark.parametrize("cfg,sd", [("c1", 1), ("c4", 4)])
+def test_capture_forward_three_replays_bit_equal_to_eager(cfg, sd):
+    """The fused call (pa_latent_forward) under the same gate and replay check."""
+    torch = _torch()
+    w = wl.make(cfg, scale_down=sd)
+    d = _dev(w)
+    before = d.key_cache.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):                         # not warmed yet: refused, nothing enqueued
+        st = _lib.pa_latent_forward(d.attrs, d.dims, d.code, d.query, d.key, d.cos, d.sin, d.slot_mapping,
+                                    d.cumseq, d.past, d.block_table, d.key_cache, d.output, d.workspace,
+                                    d.ws_bytes, check=False)
+    assert st == _lib.PA_ERR_CAPTURE_NOT_WARMED
+    del g
+    d.forward()
+    torch.cuda.synchronize()
+    eager_out, eager_cache = _bits(d.output), _bits(d.key_cache)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.forward()
+    for rep in range(3):
+        d.key_cache.copy_(before)                     # eager work between replays
+        d.output.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(d.key_cache), eager_cache), f"replay {rep}: cache differs"
+        assert np.array_equal(_bits(d.output), eager_out), f"replay {rep}: output differs"
+    del g
+
+
 def test_capture_of_an_unwarmed_signature_is_refused():
     torch = _torch()
     spec = wl.Spec(name="unwarmed", dtype="bf16", past=[7, 31], new=[3, 1], num_heads=5, head_size=64,

@@ -71,6 +71,40 @@ def test_parity_full_size(cfg):
     print(f"[result] {cfg} full, {w['dims']['token_count']} tokens: max-abs {mx:.3e} rel {rel:.3e}", flush=True)
 
 
+# The fused call (pa_latent_forward: write rows inside the attention phase's
+# first launch) against the two calls in order: bit-identical cache and output.
+@pytest.mark.parametrize("cfg,sd", SMALL + [("c4", 1)], ids=[f"{c}/{s}" for c, s in SMALL + [("c4", 1)]])
+def test_forward_bit_identical_to_write_then_attention(cfg, sd):
+    torch = _torch()
+    w = wl.make(cfg, scale_down=sd)
+    a = _dev(w)
+    b = _dev(w)
+    a.write()
+    a.attention()
+    b.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cache_bits(), b.cache_bits()), f"{cfg}/{sd}: cache differs"
+    ao = a.output.view(torch.int16).cpu().numpy()
+    bo = b.output.view(torch.int16).cpu().numpy()
+    assert np.array_equal(ao, bo), f"{cfg}/{sd}: output differs"
+    print(f"[result] {cfg}/{sd}: forward bit-identical to write + attention", flush=True)
+
+
+def test_forward_full_size_against_oracle():
+    """The benchmark's step (the fused call) on the full DeepSeek-V3 decode batch."""
+    torch = _torch()
+    w = wl.make("c4")
+    d = _dev(w)
+    before = w["key_cache"].copy()
+    d.forward()
+    torch.cuda.synchronize()
+    ref_cache, ref_out = parity.oracle(w)
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    mx, rel = parity.check_output(w["dtype"], d.output_f64(), ref_out, what="c4 forward",
+                                  heads=w["attrs"]["num_heads"])
+    print(f"[result] c4 forward: max-abs {mx:.3e} rel {rel:.3e}", flush=True)
+
+
 # ---------------------------------------------------------------------------
 # Invariants
 # ---------------------------------------------------------------------------
