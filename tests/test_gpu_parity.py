@@ -382,3 +382,63 @@ def test_workspace_too_small():
                                   d.past, d.block_table, d.output, d.workspace, d.ws_bytes - 256,
                                   check=False)
     assert st == _lib.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+# ---------------------------------------------------------------------------
+# Seeded random geometries: head sizes inside every compiled bucket (padded
+# instances included), head counts, block sizes, ragged batches with empty
+# sequences, windows, softcaps, rotary modes and dropped slots, each checked
+# element by element against the oracle through the fused call.
+# ---------------------------------------------------------------------------
+
+def _random_spec(seed):
+    r = np.random.default_rng(7000 + seed)
+    bucket = seed % 3
+    if bucket == 0:
+        hs = int(r.choice([16, 32, 48, 64]))
+        vhs = int(r.integers(1, min(hs, 32) + 1))
+        heads = int(r.integers(1, 21))
+        past_hi, new_hi = 300, 40
+    elif bucket == 1:
+        hs = int(r.choice([80, 96, 128, 144, 176, 192]))
+        vhs = int(r.integers(1, min(hs, 128) + 1))
+        heads = int(r.choice([1, 3, 8, 16, 20, 64]))
+        past_hi, new_hi = 300, 40
+    else:
+        hs = int(r.choice([208, 256, 384, 512, 576]))
+        vhs = int(r.integers(1, min(hs, 512) + 1))
+        heads = int(r.choice([1, 5, 16, 128]))
+        past_hi, new_hi = 200, 24 if heads < 128 else 2
+    do_rotary = int(r.random() < 0.7)
+    rd = ro = 0
+    if do_rotary:
+        rd = 16 * int(r.integers(1, min(hs, 128) // 16 + 1))
+        ro = 8 * int(r.integers(0, (hs - rd) // 8 + 1))
+    B = int(r.integers(1, 6))
+    past = [int(x) for x in r.integers(0, past_hi + 1, size=B)]
+    new = [int(x) for x in r.integers(0, new_hi + 1, size=B)]
+    if sum(new) == 0:
+        new[0] = 1
+    return wl.Spec(name=f"random{seed}_{hs}_{vhs}_h{heads}", dtype=str(r.choice(["f16", "bf16"])), past=past,
+                   new=new, num_heads=heads, head_size=hs, v_head_size=vhs, rotary_dim=rd, rotary_offset=ro,
+                   do_rotary=do_rotary, rotary_interleaved=int(r.random() < 0.5),
+                   block_size=int(r.choice([16, 32, 64, 128])),
+                   scale=float(r.uniform(0.5, 1.5) / math.sqrt(hs)),
+                   softcap=float(r.uniform(1.0, 30.0)) if r.random() < 0.3 else 0.0,
+                   local_window_size=int(r.integers(0, 64)) if r.random() < 0.4 else -1,
+                   slot_drop_frac=0.1 if r.random() < 0.3 else 0.0, seed=100 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_geometry(seed):
+    torch = _torch()
+    spec = _random_spec(seed)
+    w = wl.build(spec)
+    d = _dev(w)
+    before = w["key_cache"].copy()
+    d.forward()
+    torch.cuda.synchronize()
+    ref_cache, ref_out = parity.oracle(w)
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    mx, rel = parity.check_output(w["dtype"], d.output_f64(), ref_out, what=spec.name, heads=spec.num_heads)
+    print(f"[result] {spec.name}: max-abs {mx:.3e} rel {rel:.3e}", flush=True)
