@@ -307,7 +307,9 @@ pa_status pa_separate_attention(const pa_latent_attrs* attrs, int32_t kv_num_hea
  * capture_support): *write_ready / *attention_ready are set to 1 when
  * pa_latent_write / pa_latent_attention with these dtype, attrs and dims have
  * completed eagerly on that device in this process (so they may be captured),
- * else 0. Returns PA_OK, or PA_ERR_INVALID_ARGUMENT for NULL arguments.
+ * else 0. (pa_latent_forward is warmed by its own eager call; a capture of an
+ * unwarmed one is refused with PA_ERR_CAPTURE_NOT_WARMED like the others.)
+ * Returns PA_OK, or PA_ERR_INVALID_ARGUMENT for NULL arguments.
  */
 pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,
                                   int device, int32_t* write_ready, int32_t* attention_ready);
