@@ -252,7 +252,7 @@ def summarize_pmc(dirs, cmd: str):
         print(f"\nCommands: {cmd}")
 
 
-def cpu_baseline(w, target_s: float):
+def cpu_baseline(w, target_s: float, single: bool = True):
     """Time the CPU oracle (write phase + attention) on the first sequences of the
     workload until about target_s seconds of work, scaled to TFLOP/s."""
     import numpy as np
@@ -285,10 +285,36 @@ def cpu_baseline(w, target_s: float):
             done_tokens += toks.size
         b += 1
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"write phase for all {w['dims']['token_count']} tokens + attention for the first {b} "
-                      f"of {B} sequences ({done_tokens} tokens), {dt:.1f} s, float64 NumPy",
-            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+    out = {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"write phase for all {w['dims']['token_count']} tokens + attention for the first {b} "
+                     f"of {B} sequences ({done_tokens} tokens), {dt:.1f} s, float64 NumPy",
+           "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+    if single:
+        # The same oracle with its BLAS pool limited to one thread, on a
+        # shorter sample (attention of the first sequences only).
+        try:
+            from threadpoolctl import threadpool_limits
+        except Exception:
+            return out
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            f1 = tok1 = 0
+            b1 = 0
+            while b1 < B and time.perf_counter() - t1 < target_s / 3:
+                toks = np.arange(cum[b1], cum[b1 + 1])
+                if toks.size:
+                    (sep.attention if separate else orc.attention)(w, *caches, tokens=toks)
+                    for t in toks:
+                        pos = int(w["past_seqlens"][b1]) + int(t - cum[b1])
+                        lo = 0 if a["local_window_size"] < 0 else max(0, pos - a["local_window_size"])
+                        f1 += 2 * (a["head_size"] + vhs) * a["num_heads"] * (pos - lo + 1)
+                    tok1 += toks.size
+                b1 += 1
+            d1 = time.perf_counter() - t1
+        out["single_thread"] = {"value": f1 / d1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                "sample": f"attention for the first {b1} of {B} sequences ({tok1} tokens), "
+                                          f"{d1:.1f} s, BLAS limited to one thread"}
+    return out
 
 
 def stats(xs):
