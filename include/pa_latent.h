@@ -12,7 +12,10 @@
  *                        place into the paged block cache at slot_mapping[t];
  *   pa_latent_attention  partial RoPE of each query head, then causal softmax
  *                        attention over the block_table-addressed latent prefix,
- *                        V = the leading v_head_size channels of the same row.
+ *                        V = the leading v_head_size channels of the same row;
+ *
+ * and pa_latent_forward runs both in one call (the write's rows ride in the
+ * read phase's first launch).
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device addresses on the current device; all tensors
