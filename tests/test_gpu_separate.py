@@ -126,3 +126,40 @@ def test_separate_block_permutation_bit_identical():
     d2, _, _ = _run(w2)
     torch.cuda.synchronize()
     assert np.array_equal(d2.output_f64(), o1)
+
+
+# Seeded random geometries of the grouped-query layout: key/value head counts
+# and group sizes, head sizes in both compiled buckets (padded ones included),
+# value sizes up to the head size, block sizes, ragged batches, windows,
+# softcaps, rotary modes and dropped slots, element by element.
+def _random_spec(seed):
+    import math
+    r = np.random.default_rng(9100 + seed)
+    kvh = int(r.choice([1, 2, 4, 8]))
+    group = int(r.choice([1, 2, 4, 8]))
+    hs = int(r.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    vhs = 8 * int(r.integers(1, hs // 8 + 1))
+    do_rotary = int(r.random() < 0.7)
+    rd = ro = 0
+    if do_rotary:
+        rd = 16 * int(r.integers(1, hs // 16 + 1))
+        ro = 8 * int(r.integers(0, (hs - rd) // 8 + 1))
+    B = int(r.integers(1, 5))
+    past = [int(x) for x in r.integers(0, 260, size=B)]
+    new = [int(x) for x in r.integers(0, 40, size=B)]
+    if sum(new) == 0:
+        new[0] = 1
+    return wl.Spec(name=f"gqa_random{seed}_{hs}_{vhs}_{kvh}x{group}", dtype=str(r.choice(["f16", "bf16"])),
+                   past=past, new=new, num_heads=kvh * group, head_size=hs, v_head_size=vhs, rotary_dim=rd,
+                   rotary_offset=ro, do_rotary=do_rotary, rotary_interleaved=int(r.random() < 0.5),
+                   block_size=int(r.choice([16, 32, 64, 128])), scale=float(r.uniform(0.5, 1.5) / math.sqrt(hs)),
+                   softcap=float(r.uniform(1.0, 30.0)) if r.random() < 0.3 else 0.0,
+                   local_window_size=int(r.integers(0, 64)) if r.random() < 0.4 else -1,
+                   slot_drop_frac=0.1 if r.random() < 0.3 else 0.0, seed=300 + seed,
+                   layout="SEPARATE", kv_num_heads=kvh)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_separate_random_geometry(seed):
+    spec = _random_spec(seed)
+    _check(wl.build(spec), what=spec.name)
