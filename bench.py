@@ -3,9 +3,9 @@
 
 A step is one pass of the whole path over one batch: the write phase (RoPE +
 scatter of the new latent rows) followed by the attention phase (on-device
-schedule, MFMA attention, split-KV combine); in the latent layout both run in
-one fused call (pa_latent_forward), whose first launch carries the write rows
-beside the schedule. The default workload is the
+schedule, MFMA attention, split-KV combine); both run in one fused call
+(pa_latent_forward, or pa_separate_forward for the grouped-query workloads),
+whose first launch carries the write rows beside the schedule. The default workload is the
 DeepSeek-V3-dims absorbed MLA decode batch: bf16, 64 sequences with one new
 token each, past lengths uniform in [4096, 16384], 128 heads, latent 576,
 value 512, rotary 64 at offset 512, block size 64, random block permutation,
@@ -64,8 +64,8 @@ def parse():
                     help="extra steps, each after a MALL flush, for per-step statistics (0: none)")
     ap.add_argument("--flush-mib", type=int, default=512, help="scratch written before each flushed step")
     ap.add_argument("--calls", default="fused", choices=["fused", "separate"],
-                    help="latent layout: a step as one fused call (pa_latent_forward) or as pa_latent_write "
-                         "followed by pa_latent_attention")
+                    help="a step as one fused call (pa_latent_forward / pa_separate_forward) or as the write "
+                         "call followed by the attention call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -326,10 +326,10 @@ def stats(xs):
 
 def step_with_events(pa, dev, s, a, b, ka, kb):
     """One step with events a/b around its attention phase and ka/kb (recorded
-    by the library on its launch stream) around the attention kernel. In the
-    latent layout the step is the fused call (pa_latent_forward: the write rows
-    run in the attention phase's first launch), so a/b bracket the whole call;
-    in the separate layout the write is its own call before a."""
+    by the library on its launch stream) around the attention kernel. By
+    default the step is the fused call (pa_latent_forward / pa_separate_forward:
+    the write rows run in the attention phase's first launch), so a/b bracket
+    the whole call; with --calls separate the write is its own call before a."""
     if not dev.fused:
         dev.write()
         a.record(s)
@@ -596,7 +596,7 @@ def main():
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "phase": dict({"what": ("attention call: schedule launch + attention kernel + combine (events around "
                                 "the call)") if not dev.fused else
-                               ("fused call (pa_latent_forward): schedule launch carrying the write rows + "
+                               ("fused call (pa_latent_forward / pa_separate_forward): schedule launch carrying the write rows + "
                                 "attention kernel + combine (events around the call)"),
                        "avg_ms": round(attn_avg_ms, 5), "ms": stats(attn_ms)},
                       **side(attn_avg_ms)),

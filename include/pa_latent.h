@@ -306,6 +306,22 @@ pa_status pa_separate_attention(const pa_latent_attrs* attrs, int32_t kv_num_hea
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * Both phases of the separate layout in one call: pa_separate_write then
+ * pa_separate_attention on the same stream (docs.rs page, host function
+ * execute), the write's key and value rows running in the read phase's first
+ * launch, as in pa_latent_forward. Results bit-identical to the two calls in
+ * that order; arguments are the union of theirs (key_cache and value_cache
+ * updated in place, then read); every check of both runs before anything is
+ * enqueued. Errors: those of pa_separate_attention and pa_separate_write.
+ */
+pa_status pa_separate_forward(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                              pa_dtype dtype, const void* query, const void* key, const void* value,
+                              const void* cos_cache, const void* sin_cache, const int32_t* slot_mapping,
+                              const int32_t* cumulative_sequence_length, const int32_t* past_seqlens,
+                              const int32_t* block_table, void* key_cache, void* value_cache, void* output,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Capture readiness of a signature on `device` (docs.rs page,
  * capture_support): *write_ready / *attention_ready are set to 1 when
  * pa_latent_write / pa_latent_attention with these dtype, attrs and dims have

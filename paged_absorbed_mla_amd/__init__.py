@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     pa_latent_abi_version, pa_latent_attention, pa_latent_attention_noalloc, pa_latent_attention_splits,
     pa_latent_capture_ready, pa_latent_forward, pa_latent_profile_next,
     pa_latent_workspace_size,
-    pa_latent_write, pa_separate_attention, pa_separate_workspace_size, pa_separate_write,
+    pa_latent_write, pa_separate_attention, pa_separate_forward, pa_separate_workspace_size, pa_separate_write,
 )

@@ -27,7 +27,7 @@ PA_BF16 = 16
 
 EXPORTED = ("pa_latent_write", "pa_latent_workspace_size", "pa_latent_attention", "pa_latent_forward",
             "pa_latent_attention_splits", "pa_latent_attention_noalloc", "pa_latent_capture_ready",
-            "pa_separate_write", "pa_separate_workspace_size", "pa_separate_attention",
+            "pa_separate_write", "pa_separate_workspace_size", "pa_separate_attention", "pa_separate_forward",
             "pa_latent_profile_next", "pa_last_error", "pa_latent_abi_version")
 
 
@@ -103,6 +103,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_separate_workspace_size.restype = ctypes.c_int
     lib.pa_separate_attention.argtypes = [A, i32, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_separate_attention.restype = ctypes.c_int
+    lib.pa_separate_forward.argtypes = [A, i32, D, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, sz, vp]
+    lib.pa_separate_forward.restype = ctypes.c_int
     lib.pa_latent_profile_next.argtypes = [vp, vp]
     lib.pa_latent_profile_next.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
@@ -234,6 +237,18 @@ def pa_separate_workspace_size(attrs, kv_num_heads, dims, dtype, device=0, check
     if check:
         _check(st)
     return out.value if st == PA_OK else -st
+
+
+def pa_separate_forward(attrs, kv_num_heads, dims, dtype, query, key, value, cos_cache, sin_cache, slot_mapping,
+                        cumulative_sequence_length, past_seqlens, block_table, key_cache, value_cache, output,
+                        workspace, workspace_bytes, stream=None, check=True):
+    lib = load()
+    st = lib.pa_separate_forward(ctypes.byref(attrs), int(kv_num_heads), ctypes.byref(dims), int(dtype), _ptr(query),
+                                 _ptr(key), _ptr(value), _ptr(cos_cache), _ptr(sin_cache), _ptr(slot_mapping),
+                                 _ptr(cumulative_sequence_length), _ptr(past_seqlens), _ptr(block_table),
+                                 _ptr(key_cache), _ptr(value_cache), _ptr(output), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream, output, query))
+    return _check(st) if check else st
 
 
 def pa_separate_attention(attrs, kv_num_heads, dims, dtype, query, key_cache, value_cache, cos_cache, sin_cache,

@@ -236,6 +236,7 @@ pa_status attention_impl(const pa_latent_attrs* attrs, const pa_latent_dims* dim
   if ((st = check_ptr(sin_cache, "sin_cache", any && g.do_rotary)) != PA_OK) return st;
   if (fw) {
     if ((st = check_ptr(fw->key, "key", any)) != PA_OK) return st;
+    if ((st = check_ptr(fw->value, "value", any && g.sep)) != PA_OK) return st;
     if ((st = check_ptr(fw->slot_mapping, "slot_mapping", any)) != PA_OK) return st;
   }
   pa::AttnConfig cfg;
@@ -369,7 +370,7 @@ pa_status pa_latent_forward(const pa_latent_attrs* attrs, const pa_latent_dims* 
                             const int32_t* slot_mapping, const int32_t* cumulative_sequence_length,
                             const int32_t* past_seqlens, const int32_t* block_table, void* key_cache, void* output,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  const pa::FusedWrite fw{key, slot_mapping, key_cache};
+  const pa::FusedWrite fw{key, slot_mapping, key_cache, nullptr, nullptr};
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, workspace, workspace_bytes, true, stream, kForward, 0,
                         nullptr, &fw);
@@ -448,6 +449,22 @@ pa_status pa_separate_attention(const pa_latent_attrs* attrs, int32_t kv_num_hea
   return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
                         past_seqlens, block_table, output, workspace, workspace_bytes, true, stream, kAttention,
                         kv_num_heads, value_cache);
+}
+
+pa_status pa_separate_forward(const pa_latent_attrs* attrs, int32_t kv_num_heads, const pa_latent_dims* dims,
+                              pa_dtype dtype, const void* query, const void* key, const void* value,
+                              const void* cos_cache, const void* sin_cache, const int32_t* slot_mapping,
+                              const int32_t* cumulative_sequence_length, const int32_t* past_seqlens,
+                              const int32_t* block_table, void* key_cache, void* value_cache, void* output,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_num_heads < 1) {
+    g_prof_ev[0] = g_prof_ev[1] = nullptr;
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_num_heads must be >= 1, got %d", kv_num_heads);
+  }
+  const pa::FusedWrite fw{key, slot_mapping, key_cache, value, value_cache};
+  return attention_impl(attrs, dims, dtype, query, key_cache, cos_cache, sin_cache, cumulative_sequence_length,
+                        past_seqlens, block_table, output, workspace, workspace_bytes, true, stream, kForward,
+                        kv_num_heads, value_cache, &fw);
 }
 
 pa_status pa_latent_capture_ready(const pa_latent_attrs* attrs, const pa_latent_dims* dims, pa_dtype dtype,

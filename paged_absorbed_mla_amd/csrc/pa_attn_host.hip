@@ -44,11 +44,14 @@ struct SchedParams {
   // Fused call (write phase in the same launch): blocks wblock0 .. wblock0 +
   // wblocks - 1 write token rows 4 (block - wblock0) .. + 3, one per wave,
   // from wkey into wcache (wslots cache rows); wblocks = 0 otherwise.
+  // In the separate layout rows T .. 2T - 1 are the value rows (wval, wvcache).
   const uint16_t* wkey;
   const int32_t* wslot;
   uint16_t* wcache;
+  const uint16_t* wval;
+  uint16_t* wvcache;
   int64_t wslots;
-  int wblock0, wblocks;
+  int wblock0, wblocks, vhs;
 };
 
 constexpr int kSchedThreads = 256;
@@ -421,15 +424,20 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
     // Write phase of a fused call: it reads none of what the schedule and the
     // query pre-pass produce, and the attention launch that reads the rows it
     // stores follows this launch on the stream.
-    const int64_t t = (int64_t)(blockIdx.x - p.wblock0) * (kSchedThreads / 64) + (threadIdx.x >> 6);
-    if (t < p.T) {
-      const int hs = p.hs;
+    const int64_t r = (int64_t)(blockIdx.x - p.wblock0) * (kSchedThreads / 64) + (threadIdx.x >> 6);
+    const bool vrow = r >= p.T;                        // separate layout: value rows after the key rows
+    const int64_t t = vrow ? r - p.T : r;
+    if (t < p.T && (!vrow || p.wval)) {
+      const uint16_t* src = vrow ? p.wval : p.wkey;
+      uint16_t* dst = vrow ? p.wvcache : p.wcache;
+      const int hw = vrow ? p.vhs : p.hs;             // channels per head; RoPE on key rows only
+      const int rot = vrow ? 0 : (p.rd > 0);
       if (p.dtype == 16)
-        write_row<BF16>(p.wkey, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, p.wcache, t, hs, hs, p.ro, p.rd,
-                        p.rd > 0, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
+        write_row<BF16>(src, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, dst, t, p.kvh * hw, hw, p.ro, p.rd,
+                        rot, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
       else
-        write_row<F16>(p.wkey, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, p.wcache, t, hs, hs, p.ro, p.rd,
-                       p.rd > 0, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
+        write_row<F16>(src, p.cos_t, p.sin_t, p.wslot, p.cumseq, p.past, dst, t, p.kvh * hw, hw, p.ro, p.rd,
+                       rot, p.interleaved, p.B, p.wslots, p.prow, threadIdx.x & 63);
     }
     return;
   }
@@ -671,9 +679,13 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.wkey = fw ? (const uint16_t*)fw->key : nullptr;
   sp.wslot = fw ? fw->slot_mapping : nullptr;
   sp.wcache = fw ? (uint16_t*)fw->key_cache : nullptr;
+  sp.wval = fw ? (const uint16_t*)fw->value : nullptr;
+  sp.wvcache = fw ? (uint16_t*)fw->value_cache : nullptr;
+  sp.vhs = g.vhs;
   sp.wslots = g.NB * g.bs;
   sp.wblock0 = (int)(1 + rope_blocks);
-  sp.wblocks = fw ? (int)((g.T + kSchedThreads / 64 - 1) / (kSchedThreads / 64)) : 0;
+  const int64_t wrows = fw ? (fw->value ? 2 * g.T : g.T) : 0;
+  sp.wblocks = (int)((wrows + kSchedThreads / 64 - 1) / (kSchedThreads / 64));
   schedule_kernel<<<(unsigned)(1 + rope_blocks + sp.wblocks), kSchedThreads, 0, stream>>>(sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

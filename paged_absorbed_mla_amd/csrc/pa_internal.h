@@ -62,11 +62,14 @@ hipError_t attn_occupancy(const CallGeom& g, const AttnConfig& cfg, int device, 
 WsLayout plan_workspace(const CallGeom& g, const AttnConfig& cfg, int num_cus, int blocks_per_cu, bool split_kv);
 
 // Write phase carried by the attention phase's schedule launch (the fused
-// call, latent layout): key rows [T, hs] into key_cache at slot_mapping.
+// call): key rows [T, kvh * hs] into key_cache at slot_mapping (RoPE per key
+// head), and in the separate layout value rows into value_cache.
 struct FusedWrite {
   const void* key;
   const int32_t* slot_mapping;
   void* key_cache;
+  const void* value;    // separate layout: value rows [T, kvh * vhs], stored unrotated (else null)
+  void* value_cache;
 };
 
 // Attention phase: schedule, attention, combine (three launches). `ev`: null, or

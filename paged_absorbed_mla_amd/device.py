@@ -64,8 +64,8 @@ class DeviceWorkload:
         vhs = a["v_head_size"] or a["head_size"]
         T = w["dims"]["token_count"]
         self.output = torch.zeros((T, a["num_heads"] * vhs), dtype=tdt, device=self.device)
-        # step() runs both phases as one fused call (latent layout only)
-        self.fused = not self.kvh
+        # step() runs both phases as one fused call
+        self.fused = True
         self.attrs = attrs_of(w)
         self.dims = dims_of(w)
         self.code = dtype_code(w["dtype"])
@@ -106,16 +106,19 @@ class DeviceWorkload:
                                                stream)
 
     def forward(self, stream=None):
-        """Write phase and attention in one call (pa_latent_forward; latent layout)."""
+        """Write phase and attention in one call (pa_latent_forward / pa_separate_forward)."""
         if self.kvh:
-            raise ValueError("the separate layout has no fused entry point")
+            return _lib.pa_separate_forward(self.attrs, self.kvh, self.dims, self.code, self.query, self.key,
+                                            self.value, self.cos, self.sin, self.slot_mapping, self.cumseq,
+                                            self.past, self.block_table, self.key_cache, self.value_cache,
+                                            self.output, self.workspace, self.ws_bytes, stream)
         return _lib.pa_latent_forward(self.attrs, self.dims, self.code, self.query, self.key, self.cos, self.sin,
                                       self.slot_mapping, self.cumseq, self.past, self.block_table,
                                       self.key_cache, self.output, self.workspace, self.ws_bytes, stream)
 
     def step(self, stream=None):
         """One pass of the whole path: write phase, then attention (one fused
-        call in the latent layout, two calls in the separate layout)."""
+        call, or the two calls when `fused` is off)."""
         if self.fused:
             self.forward(stream)
         else:

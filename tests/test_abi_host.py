@@ -235,6 +235,17 @@ def test_separate_accepts_valid_ratios(H, kvh):
     assert "workspace" in pa.pa_last_error()
 
 
+def test_separate_forward_rejects_null_value_and_bad_ratio():
+    a = glm_attrs(num_heads=8, head_size=128, v_head_size=128, rotary_offset=64, has_scale=0)
+    D = DUMMY
+    st = pa.pa_separate_forward(a, 2, dims(), pa.PA_BF16, D, D, None, D, D, D, D, D, D, D, D, D, D, 1 << 30,
+                                stream=0, check=False)
+    assert st == pa.PA_ERR_INVALID_ARGUMENT and "value" in pa.pa_last_error()
+    st = pa.pa_separate_forward(a, 3, dims(), pa.PA_BF16, D, D, D, D, D, D, D, D, D, D, D, D, D, 1 << 30,
+                                stream=0, check=False)
+    assert st == pa.PA_ERR_INVALID_ARGUMENT
+
+
 def test_separate_needs_value_inputs():
     assert sep_attn(gqa_attrs(), 8, ptrs={"value_cache": None}) == pa.PA_ERR_INVALID_ARGUMENT
     assert "value_cache" in pa.pa_last_error()

@@ -163,3 +163,21 @@ def _random_spec(seed):
 def test_separate_random_geometry(seed):
     spec = _random_spec(seed)
     _check(wl.build(spec), what=spec.name)
+
+
+@pytest.mark.parametrize("cfg,sd", SMALL, ids=[f"{c}/{s}" for c, s in SMALL])
+def test_separate_forward_bit_identical_to_write_then_attention(cfg, sd):
+    """pa_separate_forward (key and value rows in the attention phase's first
+    launch) against pa_separate_write + pa_separate_attention."""
+    torch = _torch()
+    from paged_absorbed_mla_amd.device import DeviceWorkload
+    w = wl.make(cfg, scale_down=sd)
+    print(f"\n[case] separate forward {cfg}/{sd} dims={w['dims']}", flush=True)
+    a, b = DeviceWorkload(w), DeviceWorkload(w)
+    a.write()
+    a.attention()
+    b.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cache_bits(), b.cache_bits()), "key cache differs"
+    assert np.array_equal(a.value_cache_bits(), b.value_cache_bits()), "value cache differs"
+    assert np.array_equal(a.output.view(torch.int16).cpu().numpy(), b.output.view(torch.int16).cpu().numpy())
