@@ -537,6 +537,11 @@ static const InstanceEntry* find_instance(int dtype, const AttnConfig& c) {
 #ifndef PA_GEN_PIECE1
 #define PA_GEN_PIECE1 2
 #endif
+// Split-KV: fewest (virtual) KV tiles a workgroup's range holds (short batches
+// get fewer, longer pieces).
+#ifndef PA_MIN_UNITS
+#define PA_MIN_UNITS 4
+#endif
 static int generic_piece_units(int nw) { return nw >= 4 ? PA_GEN_PIECE4 : PA_GEN_PIECE1; }
 
 bool choose_config(const CallGeom& g, AttnConfig* cfg) {
@@ -653,7 +658,7 @@ hipError_t launch_attention(const CallGeom& g, const AttnConfig& cfg, const WsLa
   sp.wg_tile = (int32_t*)(wsb + ws.off_wg_tile);
   sp.sched = (int32_t*)(wsb + ws.off_sched);
   sp.piece_units = split_kv ? cfg.piece_units : 0;
-  sp.min_units = 4;
+  sp.min_units = PA_MIN_UNITS;
   sp.mt = (MTile*)(wsb + ws.off_mtiles);
   sp.query = (const uint16_t*)query;
   sp.cos_t = (const uint16_t*)cos_t;
