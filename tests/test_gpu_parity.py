@@ -323,11 +323,19 @@ def test_schedule_in_global_scratch():
     # B sequences and M query tiles of 32 rows; its LDS array holds 12,288.
     T, H = w["dims"]["token_count"], spec.num_heads
     assert 3 * n + 9 * ((T * H + 31) // 32 + min(n, T)) > 12288
-    _, ref_out = parity.oracle(w)
+    ref_cache, ref_out = parity.oracle(w)
     for split_kv in (True, False):
         d, _ = _run(w, split_kv=split_kv)
         parity.check_output(w["dtype"], d.output_f64(), ref_out, what=f"many_sequences split_kv={split_kv}",
                             heads=spec.num_heads)
+    # The fused call: 1,500 write rows ride in the same launch as the
+    # workspace-built schedule.
+    d = _dev(w)
+    before = w["key_cache"].copy()
+    d.forward()
+    _torch().cuda.synchronize()
+    parity.check_write(w, d.cache_bits(), ref_cache, before)
+    parity.check_output(w["dtype"], d.output_f64(), ref_out, what="many_sequences fused", heads=spec.num_heads)
 
 
 @pytest.mark.parametrize("geom", ["64_32", "192_128", "576_512"])
