@@ -150,3 +150,39 @@ def test_capture_separate_layout_three_replays_bit_equal_to_eager():
                                         d.ws_bytes, check=False)
     assert st == _lib.PA_ERR_CAPTURE_NOT_WARMED
     del g2
+
+
+def test_capture_separate_forward_three_replays_bit_equal_to_two_calls():
+    """The separate layout's fused call (pa_separate_forward), warmed eagerly,
+    captured and replayed three times: every replay bit-equal to the eager
+    write then attention."""
+    torch = _torch()
+    w = wl.make("gqa_decode", scale_down=4)
+    d = _dev(w)
+    before_k, before_v = d.key_cache.clone(), d.value_cache.clone()
+    d.write()
+    d.attention()
+    torch.cuda.synchronize()
+    eager = (_bits(d.output), _bits(d.key_cache), _bits(d.value_cache))
+    d.key_cache.copy_(before_k)
+    d.value_cache.copy_(before_v)
+    d.output.fill_(float("nan"))
+    d.forward()
+    torch.cuda.synchronize()
+    got = (_bits(d.output), _bits(d.key_cache), _bits(d.value_cache))
+    for name, a, b in zip(("output", "key cache", "value cache"), got, eager):
+        assert np.array_equal(a, b), f"eager fused call: {name} differs from the two calls"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.forward()
+    for rep in range(3):
+        d.key_cache.copy_(before_k)
+        d.value_cache.copy_(before_v)
+        d.output.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (_bits(d.output), _bits(d.key_cache), _bits(d.value_cache))
+        for name, a, b in zip(("output", "key cache", "value cache"), got, eager):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs"
+    del g
