@@ -519,7 +519,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is single-device; "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+              "no sharding or collectives are built.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -71,7 +71,7 @@ extern "C" {
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,    /* schema / geometry violation                      */
-  PA_ERR_NOT_IMPLEMENTED = 2,     /* valid request outside what this build implements */
+  PA_ERR_NOT_IMPLEMENTED = 2,     /* valid request the library does not implement     */
   PA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < pa_latent_workspace_size(...)  */
   PA_ERR_DEVICE = 4,              /* a HIP runtime call failed                        */
   PA_ERR_CAPTURE_NOT_WARMED = 5   /* stream capture of a signature not yet run eagerly */
